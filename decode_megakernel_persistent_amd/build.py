@@ -1,0 +1,82 @@
+"""Build libmk.so (the C-ABI library) for gfx950, in-tree.
+
+    python -m decode_megakernel_persistent_amd.build
+
+Every call compiles from scratch: hipcc for the HIP translation unit (device
+code plus the host runtime), g++ for the host-only compiler / simulator /
+checker, linked by hipcc into ``decode_megakernel_persistent_amd/libmk.so``.
+Also builds a host-only protocol simulator executable under ThreadSanitizer
+(``_build/mk_sim_tsan``) when requested.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmk.so")
+ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 instructions are disabled for all device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-pthread", "-Wall"]
+HOST_SRCS = ["graph.cpp", "sim.cpp"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False, tsan: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", CSRC]
+    jobs = []
+    objs = []
+    for src in HOST_SRCS:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        jobs.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    hobj = os.path.join(BUILD, "runtime.o")
+    jobs.append([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "runtime.hip"), "-o", hobj])
+    objs.append(hobj)
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-pthread", "-ldl"], verbose)
+    os.replace(tmp, LIB)
+    if tsan:
+        build_tsan(verbose)
+    return LIB
+
+
+def build_tsan(verbose: bool = False) -> str:
+    """Host-only simulator + checker executable built with ThreadSanitizer."""
+    os.makedirs(BUILD, exist_ok=True)
+    exe = os.path.join(BUILD, "mk_sim_tsan")
+    srcs = [os.path.join(CSRC, s) for s in HOST_SRCS] + [os.path.join(CSRC, "sim_main.cpp")]
+    _run(["g++", "-O1", "-g", "-std=c++17", "-pthread", "-fsanitize=thread", "-I", INCLUDE, "-I", CSRC, *srcs,
+          "-o", exe], verbose)
+    return exe
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv, tsan="--tsan" in sys.argv))

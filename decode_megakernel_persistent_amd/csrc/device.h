@@ -1,0 +1,692 @@
+// device.h - CDNA4 (gfx950) device side: event protocol, tagged activations
+// and the task bodies.  Included by runtime.hip only.
+//
+// Coherence on MI355X: the eight XCD L2 caches are not coherent with each
+// other, and whole-L2 write-back/invalidate at every release/acquire costs tens
+// of microseconds per event hop.  So no task publishes data through release/
+// acquire fences.  Instead every inter-task activation is a 64-bit word
+// (fp32 value, 32-bit step tag) written with an agent-scope relaxed atomic
+// store; a reader accepts a word only when its tag is the current step's and
+// otherwise re-reads it with agent-scope loads.  A single 64-bit atomic word
+// cannot be torn, so value and tag always travel together, and the event
+// counters (relaxed agent-scope atomics, eight sub-counters per event on
+// separate 128-byte lines) only tell a task when its inputs are ready to read.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk.h"
+#include "tables.h"
+
+namespace mk {
+
+#define DEV __device__ __forceinline__
+
+typedef uint32_t u32;
+typedef uint64_t u64;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NT = 512;       // threads per worker workgroup (8 wavefronts)
+constexpr int NWAVE = NT / 64;
+constexpr u32 OOB = 0x80000000u;  // buffer offset beyond every tile: the load returns zeros
+constexpr int AUX_NT = 2;         // non-temporal hint for streamed weights
+
+// Arguments of one step, identical for every launch of the step.
+struct StepArgs {
+  const Geom* geom;
+  const OpDesc* ops;
+  const Task* tasks;
+  const Event* events;
+  const int32_t* wl_off;
+  const int32_t* wl_ids;
+  u32* counters;
+  u32* status;
+  const int32_t* tokens;
+  const int32_t* positions;
+  uint16_t* kv_k;
+  uint16_t* kv_v;
+  float* logits;
+  mk_trace_rec* trace;
+  u64 budget;       // wall-clock ticks any single wait may take
+  u32 epoch;        // counted steps since the last reset: targets are need * (epoch + 1)
+  u32 tag;          // data tag of this step (never 0)
+  u32 magic;
+  int32_t trace_on;
+  int32_t lpt_first;  // launch-per-task: first task id of the launch
+  int32_t n_workers;
+};
+
+// ---------------------------------------------------------------- scalars
+DEV float bf_lo(u32 v) { return __uint_as_float(v << 16); }
+DEV float bf_hi(u32 v) { return __uint_as_float(v & 0xffff0000u); }
+DEV float bf2f(uint16_t b) { return __uint_as_float((u32)b << 16); }
+DEV uint16_t f2bf(float f) {
+  u32 x = __float_as_uint(f);
+  if ((x & 0x7f800000u) == 0x7f800000u) return (uint16_t)((x >> 16) | ((x & 0xffffu) ? 0x40u : 0u));
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------- tagged words
+DEV u64 pack(float v, u32 tag) { return ((u64)tag << 32) | (u64)__float_as_uint(v); }
+DEV void st_t(u64* p, float v, u32 tag) {
+  __hip_atomic_store(p, pack(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __noinline__ u64 ld_t_slow(const u64* p, u32 tag, u64 budget, u32* status) {
+  const u64 t0 = wall_clock64();
+  for (int i = 0;; ++i) {
+    u64 w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((u32)(w >> 32) == tag) return w;
+    if ((i & 7) == 7) {
+      if (__hip_atomic_load(status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+          wall_clock64() - t0 > budget) {
+        u32 z = 0;
+        if (__hip_atomic_compare_exchange_strong(status + ST_ERROR, &z, (u32)ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          __hip_atomic_store(status + ST_TASK, 0xFFFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(status + ST_SEEN, (u32)(w >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(status + ST_TARGET, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(status + ST_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return pack(0.0f, tag);
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Fast path: a workgroup-scope relaxed load (a plain cached load: one fetch
+// per XCD, shared through its L2); fall back when the tag is stale.
+DEV float ld_t(const u64* p, const StepArgs& a) {
+  u64 w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if ((u32)(w >> 32) != a.tag) w = ld_t_slow(p, a.tag, a.budget, a.status);
+  return __uint_as_float((u32)w);
+}
+
+// ---------------------------------------------------------------- reductions
+DEV float dpp_f(float v, int ctrl);
+template <int CTRL>
+DEV float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over each 16-lane row (result in every lane of the row).
+DEV float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  return v;
+}
+DEV float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  return v;
+}
+DEV float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+// Whole-wavefront sum / max, uniform result.  Call with all 64 lanes active.
+DEV float wave_sum(float v) {
+  v = row16_sum(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+DEV float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+// ---------------------------------------------------------------- task context
+struct Ctx {
+  const StepArgs* a;
+  Task t;
+  int id;
+  int agent;     // worker index, or -1 in launch-per-task mode
+  bool lpt;
+  char* lds;     // dynamic LDS (kLdsBytes)
+  int* flags;    // small static LDS block: [0] abort, [1] seen, [2] start ticket, [3] start clock
+};
+
+DEV u32 event_total(const StepArgs& a, int ev, int lane) {
+  u32 v = 0;
+  if (lane < kSubCounters)
+    v = __hip_atomic_load(a.counters + ((size_t)ev * kSubCounters + lane) * kCounterStride, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return (u32)__builtin_amdgcn_readlane((int)v, 0);
+}
+
+DEV void report_timeout(const StepArgs& a, int task, int ev, u32 seen, u32 target) {
+  u32 z = 0;
+  if (__hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(a.status + ST_TASK, (u32)task, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.status + ST_EVENT, (u32)ev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.status + ST_SEEN, seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.status + ST_TARGET, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __hip_atomic_store(a.status + ST_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for the task's dependency event (wavefront 0 polls, the others wait at
+// the barrier), then take the trace start ticket.  All threads call this.
+DEV void wait_dep(Ctx& c) {
+  const StepArgs& a = *c.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ev = c.t.dep;
+  if (tid < 64) {
+    u32 seen = 0;
+    int bad = 0;
+    if (ev >= 0) {
+      const u32 target = (u32)a.events[ev].need * (a.epoch + 1u);
+      seen = event_total(a, ev, lane);
+      if (!c.lpt) {
+        const u64 t0 = wall_clock64();
+        int polls = 0;
+        while (seen < target) {
+          __builtin_amdgcn_s_sleep(1);
+          if ((++polls & 31) == 0) {
+            if (__hip_atomic_load(a.status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+                wall_clock64() - t0 > a.budget) {
+              if (lane == 0) report_timeout(a, c.id, ev, seen, target);
+              bad = 1;
+              break;
+            }
+          }
+          seen = event_total(a, ev, lane);
+        }
+      }
+    }
+    if (lane == 0) {
+      c.flags[1] = (int)seen;
+      if (bad) c.flags[0] = 1;
+      if (a.trace_on) {
+        c.flags[2] = (int)__hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        c.flags[3] = (int)(u32)wall_clock64();
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// All threads: make this thread's stores complete, then one thread records
+// the trace and triggers the task's event.
+DEV void finish(Ctx& c) {
+  const StepArgs& a = *c.a;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (a.trace_on && !c.flags[0]) {
+      u32 te = __hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      u32 slot = __hip_atomic_fetch_add(a.status + ST_TRACE_N, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (slot < (u32)a.geom->n_tasks) {
+        mk_trace_rec r;
+        r.task = c.id;
+        r.worker = (int16_t)c.agent;
+        r.xcc = (int16_t)(__builtin_amdgcn_s_getreg(6164) & 0xF);  // HW_REG_XCC_ID[3:0]
+        r.t_start = (u32)c.flags[2];
+        r.t_end = te;
+        r.dep_seen = (u32)c.flags[1];
+        r.step = a.epoch;
+        r.clk_start = (u32)c.flags[3];
+        r.clk_end = (u32)wall_clock64();
+        a.trace[slot] = r;
+      }
+    }
+    if (c.t.trig >= 0 && !c.flags[0]) {
+      const int sub = (c.agent >= 0 ? c.agent : (int)blockIdx.x) & (kSubCounters - 1);
+      __hip_atomic_fetch_add(a.counters + ((size_t)c.t.trig * kSubCounters + sub) * kCounterStride, 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Block-wide sum of one value per thread for NB independent values.
+template <int NB>
+DEV void block_sum(float (&v)[NB], float* red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float s = wave_sum(v[b]);
+    if (lane == 0) red[b * NWAVE + wave] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) s += red[b * NWAVE + w];
+    v[b] = s;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- embedding
+DEV void body_embed(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int b = c.t.a0, H = G.H;
+  int tok = a.tokens[b];
+  if (tok < 0 || tok >= G.V) {
+    if (threadIdx.x == 0) {
+      u32 z = 0;
+      __hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_BAD_INPUT, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    tok = 0;
+  }
+  const uint16_t* row = op.w + (size_t)tok * H;
+  for (int k = threadIdx.x; k < H; k += NT) st_t(op.out + (size_t)b * H + k, bf2f(row[k]), a.tag);
+}
+
+// ---------------------------------------------------------------- GEMV input staging
+// xs[b][k] = in[b][k], or rmsnorm(in[b]) * g when the op normalises its input.
+template <int NB>
+DEV void stage_input(Ctx& c, const OpDesc& op, float* xs, float* red) {
+  const StepArgs& a = *c.a;
+  const int K = op.K;
+  float ss[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    ss[b] = 0.f;
+    const u64* in = op.in + (size_t)b * K;
+    for (int k = threadIdx.x; k < K; k += NT) {
+      float v = ld_t(in + k, a);
+      xs[b * K + k] = v;
+      ss[b] += v * v;
+    }
+  }
+  if (op.norm_in) {
+    block_sum<NB>(ss, red);
+    const float eps = a.geom->eps;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float r = rsqrtf(ss[b] / (float)K + eps);
+      for (int k = threadIdx.x; k < K; k += NT) xs[b * K + k] = xs[b * K + k] * r * op.g[k];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- GEMV epilogue
+template <int NB>
+DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR) {
+  const StepArgs& a = *c.a;
+  const int nr = c.t.a2, r0 = c.t.a1, N = op.N;
+  for (int j = threadIdx.x; j < NB * nr; j += NT) {
+    const int b = j / nr, r = j - b * nr, row = r0 + r;
+    const float v = rsl[b * NR + r];
+    switch (op.kind) {
+      case OP_QKV:
+      case OP_ROUTER:
+        st_t(op.out + (size_t)b * N + row, v, a.tag);
+        break;
+      case OP_OPROJ:
+      case OP_DOWN:
+        st_t(op.out + (size_t)b * N + row, ld_t(op.res + (size_t)b * N + row, a) + v, a.tag);
+        break;
+      case OP_GATEUP:
+        st_t(op.out + (size_t)b * N + row, silu(v) * rsl[b * NR + nr + r], a.tag);
+        break;
+      case OP_LMHEAD:
+        a.logits[(size_t)b * N + row] = v;
+        break;
+      default:
+        break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- GEMV (VALU, batch <= 4)
+// Tile = NR contiguous bf16 rows of length K.  Wavefront w owns rows w, w+8, ...;
+// in each row lane l reads 16-byte chunks l, l+64, ... (1 KB coalesced per
+// wavefront load).  A row is cut into segments of S chunks per lane; a ring of
+// DEPTH segments keeps about 32 loads per lane in flight, and the first DEPTH
+// segments are issued before the dependency wait.  Loads go through a buffer
+// resource so out-of-range segments return zeros without touching memory.
+template <int NB, int S>
+DEV void gemv_valu(Ctx& c, const OpDesc& op) {
+  constexpr int DEPTH = S >= 8 ? 4 : S >= 6 ? 5 : S >= 4 ? 8 : S >= 3 ? 10 : S >= 2 ? 16 : 32;
+  const Task& t = c.t;
+  const int K = op.K, CPR = K >> 3, NCH = (CPR + 63) >> 6, SPR = NCH / S;
+  const bool gu = op.kind == OP_GATEUP;
+  const int NR = gu ? 2 * t.a2 : t.a2;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nrw = NR > wave ? (NR - wave + NWAVE - 1) / NWAVE : 0;
+  const int NSEG = nrw * SPR;
+  const uint16_t* Wt = op.w + (size_t)(u32)t.a3;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, (int)((u32)NR * (u32)K * 2u), 0x00020000);
+
+  u32x4 buf[DEPTH][S];
+  // segment (fi, fq) of the refill cursor
+  int fi = 0, fq = 0;
+  auto voff = [&](int i, int q, int u) -> u32 {
+    const int cc = (q * S + u) * 64 + lane;
+    if (i >= nrw || cc >= CPR) return OOB;
+    return (u32)((wave + NWAVE * i) * K + cc * 8) * 2u;
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) buf[d][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff(fi, fq, u), 0, AUX_NT);
+    if (++fq == SPR) { fq = 0; ++fi; }
+  }
+
+  wait_dep(c);
+  float* xs = (float*)c.lds;
+  float* rsl = xs + kStageFloats;
+  float* red = (float*)(c.flags + 8);
+  stage_input<NB>(c, op, xs, red);
+  __syncthreads();
+
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  int ci = 0, cq = 0;  // consume cursor
+  for (int s0 = 0; s0 < NSEG; s0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (s0 + d < NSEG) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+          const int cc = (cq * S + u) * 64 + lane;
+          if (cc < CPR) {
+            const u32x4 w = buf[d][u];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const f32x4 x0 = *(const f32x4*)(xs + b * K + cc * 8);
+              const f32x4 x1 = *(const f32x4*)(xs + b * K + cc * 8 + 4);
+              float s = acc[b];
+              s = fmaf(bf_lo(w.x), x0.x, s);
+              s = fmaf(bf_hi(w.x), x0.y, s);
+              s = fmaf(bf_lo(w.y), x0.z, s);
+              s = fmaf(bf_hi(w.y), x0.w, s);
+              s = fmaf(bf_lo(w.z), x1.x, s);
+              s = fmaf(bf_hi(w.z), x1.y, s);
+              s = fmaf(bf_lo(w.w), x1.z, s);
+              s = fmaf(bf_hi(w.w), x1.w, s);
+              acc[b] = s;
+            }
+          }
+        }
+        if (cq == SPR - 1) {
+          const int r = wave + NWAVE * ci;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const float v = wave_sum(acc[b]);
+            if (lane == 0) rsl[b * NR + r] = v;
+            acc[b] = 0.f;
+          }
+        }
+        if (++cq == SPR) { cq = 0; ++ci; }
+      }
+#pragma unroll
+      for (int u = 0; u < S; ++u) buf[d][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff(fi, fq, u), 0, AUX_NT);
+      if (++fq == SPR) { fq = 0; ++fi; }
+    }
+  }
+  __syncthreads();
+  gemv_epilogue<NB>(c, op, rsl, NR);
+}
+
+template <int NB>
+DEV void gemv_valu_any(Ctx& c, const OpDesc& op) {
+  const int nch = ((op.K >> 3) + 63) >> 6;
+  if (nch % 8 == 0) gemv_valu<NB, 8>(c, op);
+  else if (nch % 6 == 0) gemv_valu<NB, 6>(c, op);
+  else if (nch % 4 == 0) gemv_valu<NB, 4>(c, op);
+  else if (nch % 3 == 0) gemv_valu<NB, 3>(c, op);
+  else if (nch % 2 == 0) gemv_valu<NB, 2>(c, op);
+  else gemv_valu<NB, 1>(c, op);
+}
+
+// ---------------------------------------------------------------- attention
+// One (sequence b, kv head g, chunk) task: q-norm + RoPE for the G query
+// heads; in the last chunk also k-norm + RoPE of the new key, bf16 rounding,
+// and the KV-cache append at position p; then scores, a chunk-local softmax
+// (max m, sum l) and the unnormalised output o for each head.
+// Rows of the chunk are read 16 bytes per lane: D/8 lanes per row.
+DEV void body_attn(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int b = c.t.a0, g = c.t.a1, ch = c.t.a2;
+  const int D = G.D, NG = G.G, C = G.C, Hkv = G.Hkv, cap = G.cap;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int pos = a.positions[b];
+  if (pos < 0 || pos >= cap) {
+    if (tid == 0) {
+      u32 z = 0;
+      __hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_BAD_INPUT, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    pos = pos < 0 ? 0 : cap - 1;
+  }
+  const int len = pos + 1;
+  const int t0 = (int)((long)ch * len / C), t1 = (int)((long)(ch + 1) * len / C);
+  const bool last = ch == C - 1;
+  const int T = t1 - t0;
+  const int Told = last ? T - 1 : T;  // rows read from the cache (the newest comes from registers)
+  const size_t base = ((((size_t)op.layer * G.B + b) * Hkv + g) * (size_t)cap) * D;
+  uint16_t* Kc = a.kv_k + base;
+  uint16_t* Vc = a.kv_v + base;
+  const int cpr = D >> 3, rpp = NT / cpr;  // lanes per row, rows per pass
+  const int my_r = tid / cpr, my_c = tid - my_r * cpr;
+  const u32 span = (u32)(Told > 0 ? Told : 0) * (u32)D * 2u;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kc + (size_t)t0 * D), 0, (int)span, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vc + (size_t)t0 * D), 0, (int)span, 0x00020000);
+  auto roff = [&](int p) -> u32 {
+    const int r = p * rpp + my_r;
+    return r < Told ? (u32)(r * D + my_c * 8) * 2u : OOB;
+  };
+  constexpr int RING = 4;
+  u32x4 kr[RING], vr[RING];
+#pragma unroll
+  for (int p = 0; p < RING; ++p) {
+    kr[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, roff(p), 0, AUX_NT);
+    vr[p] = __builtin_amdgcn_raw_buffer_load_b128(rv, roff(p), 0, AUX_NT);
+  }
+
+  wait_dep(c);
+
+  float* qs = (float*)c.lds;                 // [NG][D], pre-scaled by 1/sqrt(D)
+  uint16_t* knew = (uint16_t*)(qs + 8 * 128);  // [D] new key (bf16 bits)
+  uint16_t* vnew = knew + 128;                 // [D] new value
+  float* sc = (float*)(vnew + 128);            // [NG][SMAX] scores, then weights
+  const int SMAX = kScoreFloats / NG;
+  float* red = sc + kScoreFloats;              // [8][NG][D]
+  float* ml = red + 8 * 8 * 128;               // [NG][2]
+
+  // q / k / v prologue: wavefront h handles head h (then k at NG, v at NG+1)
+  const u64* qkv = op.in + (size_t)b * G.qkv_stride + (size_t)g * (NG + 2) * D;
+  const int half = D >> 1;
+  for (int h = wave; h < NG + 2; h += NWAVE) {
+    if (h >= NG && !last) continue;
+    float x0 = 0.f, x1 = 0.f;
+    if (lane < half) {
+      x0 = ld_t(qkv + (size_t)h * D + lane, a);
+      x1 = ld_t(qkv + (size_t)h * D + lane + half, a);
+    }
+    if (h == NG + 1) {
+      if (lane < half) {
+        const uint16_t v0 = f2bf(x0), v1 = f2bf(x1);
+        Vc[(size_t)pos * D + lane] = v0;
+        Vc[(size_t)pos * D + lane + half] = v1;
+        vnew[lane] = v0;
+        vnew[lane + half] = v1;
+      }
+      continue;
+    }
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float r = rsqrtf(ss / (float)D + G.eps);
+    if (lane < half) {
+      const float* gain = h < NG ? op.g : op.g2;
+      x0 *= r * gain[lane];
+      x1 *= r * gain[lane + half];
+      double sn, cs;
+      sincos((double)pos * G.inv_freq[lane], &sn, &cs);
+      const float cf = (float)cs, sf = (float)sn;
+      const float y0 = x0 * cf - x1 * sf, y1 = x1 * cf + x0 * sf;
+      if (h < NG) {
+        qs[h * D + lane] = y0 * G.attn_scale;
+        qs[h * D + lane + half] = y1 * G.attn_scale;
+      } else {
+        const uint16_t k0 = f2bf(y0), k1 = f2bf(y1);
+        Kc[(size_t)pos * D + lane] = k0;
+        Kc[(size_t)pos * D + lane + half] = k1;
+        knew[lane] = k0;
+        knew[lane + half] = k1;
+      }
+    }
+  }
+  __syncthreads();
+
+  // scores s[h][r] = q_h . K_r  (q already scaled)
+  const int npass = (T + rpp - 1) / rpp;
+  for (int p0 = 0; p0 < npass; p0 += RING) {
+#pragma unroll
+    for (int d = 0; d < RING; ++d) {
+      const int p = p0 + d;
+      if (p < npass) {
+        const int r = p * rpp + my_r;
+        u32x4 k = kr[d];
+        if (last && r == T - 1) k = *(const u32x4*)(knew + my_c * 8);
+        float part[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          part[h] = 0.f;
+          if (h < NG) {
+            const f32x4 q0 = *(const f32x4*)(qs + h * D + my_c * 8);
+            const f32x4 q1 = *(const f32x4*)(qs + h * D + my_c * 8 + 4);
+            float s = bf_lo(k.x) * q0.x;
+            s = fmaf(bf_hi(k.x), q0.y, s);
+            s = fmaf(bf_lo(k.y), q0.z, s);
+            s = fmaf(bf_hi(k.y), q0.w, s);
+            s = fmaf(bf_lo(k.z), q1.x, s);
+            s = fmaf(bf_hi(k.z), q1.y, s);
+            s = fmaf(bf_lo(k.w), q1.z, s);
+            s = fmaf(bf_hi(k.w), q1.w, s);
+            part[h] = s;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          if (h < NG) {
+            float s = part[h];
+            for (int o = 1; o < cpr; o <<= 1) s += __shfl_xor(s, o);
+            if (my_c == 0 && r < T) sc[h * SMAX + r] = s;
+          }
+        }
+      }
+      kr[d] = __builtin_amdgcn_raw_buffer_load_b128(rk, roff(p + RING), 0, AUX_NT);
+    }
+  }
+  __syncthreads();
+  // chunk-local softmax per head
+  for (int h = wave; h < NG; h += NWAVE) {
+    float m = -INFINITY;
+    for (int r = lane; r < T; r += 64) m = fmaxf(m, sc[h * SMAX + r]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int r = lane; r < T; r += 64) {
+      const float e = expf(sc[h * SMAX + r] - m);
+      sc[h * SMAX + r] = e;
+      l += e;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      ml[2 * h] = m;
+      ml[2 * h + 1] = l;
+    }
+  }
+  __syncthreads();
+  // o[h][d] = sum_r w[h][r] V_r[d]
+  float o[8][8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
+  for (int p0 = 0; p0 < npass; p0 += RING) {
+#pragma unroll
+    for (int d = 0; d < RING; ++d) {
+      const int p = p0 + d;
+      if (p < npass) {
+        const int r = p * rpp + my_r;
+        if (r < T) {
+          u32x4 v = vr[d];
+          if (last && r == T - 1) v = *(const u32x4*)(vnew + my_c * 8);
+          const float vv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                               bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+#pragma unroll
+          for (int h = 0; h < 8; ++h)
+            if (h < NG) {
+              const float w = sc[h * SMAX + r];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) o[h][j] = fmaf(w, vv[j], o[h][j]);
+            }
+        }
+      }
+      vr[d] = __builtin_amdgcn_raw_buffer_load_b128(rv, roff(p + RING), 0, AUX_NT);
+    }
+  }
+  // reduce over the rows of a pass: lanes that share my_c within the wavefront, then across wavefronts
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    if (h < NG)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float s = o[h][j];
+        for (int off = cpr; off < 64; off <<= 1) s += __shfl_xor(s, off);
+        o[h][j] = s;
+      }
+  if (lane < cpr) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      if (h < NG)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[(wave * NG + h) * D + lane * 8 + j] = o[h][j];
+  }
+  __syncthreads();
+  u64* part = op.out + ((((size_t)b * Hkv + g) * C + ch) * NG) * (size_t)(D + 2);
+  for (int j = tid; j < NG * D; j += NT) {
+    const int h = j / D, dd = j - h * D;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) s += red[(w * NG + h) * D + dd];
+    st_t(part + (size_t)h * (D + 2) + 2 + dd, s, a.tag);
+  }
+  if (tid < NG) {
+    st_t(part + (size_t)tid * (D + 2), ml[2 * tid], a.tag);
+    st_t(part + (size_t)tid * (D + 2) + 1, ml[2 * tid + 1], a.tag);
+  }
+}
+
+// ---------------------------------------------------------------- merge
+// attn[b][g*G+h][d] = sum_c e^{m_c - M} o_c[d] / sum_c e^{m_c - M} l_c
+DEV void body_merge(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int b = c.t.a0, g = c.t.a1;
+  const int D = G.D, NG = G.G, C = G.C;
+  const u64* part = op.in + (((size_t)b * G.Hkv + g) * C) * NG * (size_t)(D + 2);
+  for (int j = threadIdx.x; j < NG * D; j += NT) {
+    const int h = j / D, dd = j - h * D;
+    float M = -INFINITY;
+    for (int ch = 0; ch < C; ++ch) M = fmaxf(M, ld_t(part + ((size_t)ch * NG + h) * (D + 2), a));
+    float L = 0.f, O = 0.f;
+    for (int ch = 0; ch < C; ++ch) {
+      const u64* p = part + ((size_t)ch * NG + h) * (D + 2);
+      const float m = ld_t(p, a);
+      if (m == -INFINITY) continue;
+      const float w = expf(m - M);
+      L = fmaf(w, ld_t(p + 1, a), L);
+      O = fmaf(w, ld_t(p + 2 + dd, a), O);
+    }
+    st_t(op.out + (size_t)b * G.Hq * D + ((size_t)g * NG + h) * D + dd, O / L, a.tag);
+  }
+}
+
+}  // namespace mk

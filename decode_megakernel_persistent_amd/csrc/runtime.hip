@@ -1,0 +1,702 @@
+// runtime.hip - kernels and the host side of the C ABI (include/mk.h).
+//
+// Persistent mode: one cooperative launch of mk_worker with one 512-thread
+// workgroup per compute unit (the 128 KB LDS request leaves room for only one
+// per CU) plus a one-wavefront mk_dispatch kernel on an internal second
+// stream, as the MPK pages split worker and scheduler kernels onto two
+// streams (page "Mirage Persistent Kernel (MPK)", section 5.1).  Each worker
+// walks its statically assigned task list in increasing id order; every task
+// issues its first weight loads, waits on its dependency event, runs its body
+// and triggers its event (MPK abstract: decentralised in-kernel scheduling;
+// review page 2512.22219, section 2.4).
+//
+// Launch-per-task mode: the same bodies, one launch of mk_lpt per
+// (event range, operator) run in BFS order; stream order replaces the waits.
+#include <dlfcn.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "device.h"
+#include "graph.h"
+
+namespace mk {
+
+// ---------------------------------------------------------------- kernels
+template <int NB>
+DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int* flags) {
+  Ctx c;
+  c.a = &a;
+  c.t = a.tasks[id];
+  c.id = id;
+  c.agent = agent;
+  c.lpt = lpt;
+  c.lds = lds;
+  c.flags = flags;
+  const OpDesc& op = a.ops[c.t.op];
+  switch (op.kind) {
+    case OP_QKV:
+    case OP_OPROJ:
+    case OP_GATEUP:
+    case OP_DOWN:
+    case OP_LMHEAD:
+    case OP_ROUTER:
+      gemv_valu_any<NB>(c, op);
+      break;
+    case OP_ATTN:
+      body_attn(c, op);
+      break;
+    case OP_MERGE:
+      wait_dep(c);
+      body_merge(c, op);
+      break;
+    case OP_EMBED:
+      wait_dep(c);
+      body_embed(c, op);
+      break;
+    default:
+      wait_dep(c);
+      break;
+  }
+  finish(c);
+}
+
+DEV bool entry_ok(const StepArgs& a, int* flags) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    if (a.geom->magic != a.magic) {
+      u32 z = 0;
+      __hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_CONFIG, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = 0;
+    }
+    // a failed step leaves the error word set until mk_check clears it
+    if (__hip_atomic_load(a.status + ST_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ok = 0;
+    flags[0] = ok ? 0 : 1;
+  }
+  __syncthreads();
+  return flags[0] == 0;
+}
+
+template <int NB>
+__global__ void __launch_bounds__(NT, 1) mk_worker(StepArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int flags[64];
+  if (entry_ok(a, flags)) {
+    const int w = blockIdx.x;
+    for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
+      run_task<NB>(a, a.wl_ids[k], w, false, lds, flags);
+      __syncthreads();
+      if (flags[0]) break;
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.status + ST_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NB>
+__global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int flags[64];
+  if (entry_ok(a, flags)) run_task<NB>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags);
+}
+
+// The dispatch wavefront: runs the dispatcher's own task list (work-list
+// routing of routed-expert layers), then watches the workers until every one
+// has finished the step, raising the abort flag if that takes longer than the
+// watchdog budget.
+__global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
+  const int W = a.n_workers;
+  const int lane = threadIdx.x;
+  const u32 target = (u32)W * (a.epoch + 1u);
+  const u64 t0 = wall_clock64();
+  (void)lane;
+  for (;;) {
+    u32 done = __hip_atomic_load(a.status + ST_DONE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done >= target) break;
+    if (__hip_atomic_load(a.status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+    if (wall_clock64() - t0 > 4 * a.budget) {
+      if (threadIdx.x == 0) report_timeout(a, -1, -1, done, target);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(127);
+  }
+}
+
+typedef void (*kernel_fn)(StepArgs);
+static const void* worker_fn(int nb) {
+  switch (nb) {
+    case 1: return (const void*)mk_worker<1>;
+    case 2: return (const void*)mk_worker<2>;
+    case 3: return (const void*)mk_worker<3>;
+    default: return (const void*)mk_worker<4>;
+  }
+}
+static const void* lpt_fn(int nb) {
+  switch (nb) {
+    case 1: return (const void*)mk_lpt<1>;
+    case 2: return (const void*)mk_lpt<2>;
+    case 3: return (const void*)mk_lpt<3>;
+    default: return (const void*)mk_lpt<4>;
+  }
+}
+
+}  // namespace mk
+
+// ==================================================================== host
+using namespace mk;
+
+namespace {
+
+#define HIPCHK(x)                                                                   \
+  do {                                                                              \
+    hipError_t e_ = (x);                                                            \
+    if (e_ != hipSuccess) {                                                         \
+      set_error(std::string(#x) + " failed: " + hipGetErrorString(e_));             \
+      return MK_ERR_HIP;                                                            \
+    }                                                                               \
+  } while (0)
+
+std::string tensor_name_list(const mk_model_shape& s, std::vector<std::pair<std::string, std::pair<int64_t, int64_t>>>* out) {
+  const int64_t H = s.hidden, D = s.head_dim, Hq = s.n_q_heads, Hkv = s.n_kv_heads;
+  auto add = [&](const std::string& n, int64_t r, int64_t c) { out->push_back({n, {r, c}}); };
+  add("embed", s.vocab, H);
+  for (int l = 0; l < s.n_layers; ++l) {
+    std::string p = "layers." + std::to_string(l) + ".";
+    add(p + "in_norm", H, 1);
+    add(p + "wq", Hq * D, H);
+    add(p + "wk", Hkv * D, H);
+    add(p + "wv", Hkv * D, H);
+    add(p + "q_norm", D, 1);
+    add(p + "k_norm", D, 1);
+    add(p + "wo", H, Hq * D);
+    add(p + "post_norm", H, 1);
+    if (s.n_experts == 0) {
+      add(p + "w_gate", s.intermediate, H);
+      add(p + "w_up", s.intermediate, H);
+      add(p + "w_down", H, s.intermediate);
+    } else {
+      add(p + "router", s.n_experts, H);
+      for (int e = 0; e < s.n_experts; ++e) {
+        std::string q = p + "experts." + std::to_string(e) + ".";
+        add(q + "w_gate", s.expert_intermediate, H);
+        add(q + "w_up", s.expert_intermediate, H);
+        add(q + "w_down", H, s.expert_intermediate);
+      }
+    }
+  }
+  add("final_norm", H, 1);
+  if (!s.tied_embeddings) add("lm_head", s.vocab, H);
+  return "";
+}
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return 0;
+  return p.multiProcessorCount;
+}
+
+}  // namespace
+
+extern "C" {
+
+mk_status mk_build_graph(const mk_model_shape* shape, int32_t batch, int32_t max_ctx, const mk_build_opts* opts,
+                         mk_graph** out) {
+  if (!shape || !out) {
+    set_error("mk_build_graph: null argument");
+    return MK_ERR_ARG;
+  }
+  *out = nullptr;
+  mk_build_opts o{};
+  if (opts) o = *opts;
+  if (o.mode != MK_PERSISTENT && o.mode != MK_LAUNCH_PER_TASK) {
+    set_error("mk_build_graph: unknown mode");
+    return MK_ERR_ARG;
+  }
+  int32_t W = o.num_workers;
+  if (W <= 0) {
+    W = device_cu_count();
+    if (W <= 0) W = 256;  // gfx950 compute units, when no device is visible
+  }
+  std::string err;
+  Graph* G = compile_decoder(*shape, batch, max_ctx, o, W, o.no_fusion == 0, &err);
+  if (!G) {
+    set_error("mk_build_graph: " + err);
+    return MK_ERR_SHAPE;
+  }
+  mk_graph* g = new mk_graph();
+  g->G = G;
+  g->mode = o.mode;
+  g->per_task_launch = o.per_task_launch;
+  *out = g;
+  return MK_OK;
+}
+
+mk_status mk_workspace_size(const mk_graph* g, size_t* arena_bytes, size_t* scratch_bytes, size_t* trace_bytes) {
+  if (!g || !g->G) {
+    set_error("mk_workspace_size: null graph");
+    return MK_ERR_ARG;
+  }
+  if (arena_bytes) *arena_bytes = (size_t)g->G->arena_bytes;
+  if (scratch_bytes) *scratch_bytes = (size_t)g->G->scratch_bytes;
+  if (trace_bytes) *trace_bytes = (size_t)g->G->trace_bytes;
+  return MK_OK;
+}
+
+mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void* d_arena, void* d_scratch,
+                          void* d_trace, void* stream_) {
+  if (!g || !g->G || (!tensors && n > 0) || !d_arena || !d_scratch) {
+    set_error("mk_load_weights: null argument");
+    return MK_ERR_ARG;
+  }
+  Graph& G = *g->G;
+  if (G.trace_bytes > 0 && !d_trace) {
+    set_error("mk_load_weights: trace buffer required (graph built with trace=1)");
+    return MK_ERR_ARG;
+  }
+  if (G.gemv == MK_GEMV_MFMA) {
+    set_error("mk_load_weights: MFMA tile layout not available in this build");
+    return MK_ERR_SHAPE;
+  }
+  hipStream_t stream = (hipStream_t)stream_;
+  // ---- the tensor set
+  std::vector<std::pair<std::string, std::pair<int64_t, int64_t>>> want;
+  tensor_name_list(G.shape, &want);
+  std::map<std::string, const mk_tensor*> have;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!tensors[i].name || !tensors[i].data) {
+      set_error("mk_load_weights: tensor with null name or data");
+      return MK_ERR_ARG;
+    }
+    if (!have.emplace(tensors[i].name, &tensors[i]).second) {
+      set_error(std::string("mk_load_weights: duplicate tensor ") + tensors[i].name);
+      return MK_ERR_ARG;
+    }
+  }
+  for (auto& w : want) {
+    auto it = have.find(w.first);
+    if (it == have.end()) {
+      set_error("mk_load_weights: missing tensor " + w.first);
+      return MK_ERR_ARG;
+    }
+    if (it->second->rows != w.second.first || it->second->cols != w.second.second) {
+      set_error("mk_load_weights: tensor " + w.first + " has shape [" + std::to_string(it->second->rows) + "," +
+                std::to_string(it->second->cols) + "], expected [" + std::to_string(w.second.first) + "," +
+                std::to_string(w.second.second) + "]");
+      return MK_ERR_ARG;
+    }
+  }
+  if ((int32_t)have.size() != (int32_t)want.size()) {
+    set_error("mk_load_weights: unexpected extra tensors");
+    return MK_ERR_ARG;
+  }
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  g->device = dev;
+  if (!g->side_stream) {
+    hipStream_t s2;
+    HIPCHK(hipStreamCreateWithFlags(&s2, hipStreamNonBlocking));
+    g->side_stream = s2;
+    hipEvent_t ea, eb;
+    HIPCHK(hipEventCreateWithFlags(&ea, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&eb, hipEventDisableTiming));
+    g->ev_a = ea;
+    g->ev_b = eb;
+  }
+  char* arena = (char*)d_arena;
+  char* scratch = (char*)d_scratch;
+  // ---- weights
+  for (const CopyJob& cj : G.copies) {
+    const mk_tensor* t = have[cj.tensor];
+    const char* src = (const char*)t->data + (size_t)cj.row0 * (size_t)t->cols * 2;
+    const size_t bytes = (size_t)cj.nrows * (size_t)t->cols * 2;
+    if (cj.kind == CopyJob::ROWS) {
+      HIPCHK(hipMemcpyAsync(arena + cj.dst, src, bytes, t->on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
+                            stream));
+    } else if (cj.kind == CopyJob::GAIN_F32) {
+      std::vector<uint16_t> hb((size_t)cj.nrows);
+      if (t->on_device) {
+        HIPCHK(hipMemcpy(hb.data(), src, bytes, hipMemcpyDeviceToHost));
+      } else {
+        std::memcpy(hb.data(), src, bytes);
+      }
+      std::vector<float> hf(hb.size());
+      for (size_t i = 0; i < hb.size(); ++i) {
+        uint32_t u = (uint32_t)hb[i] << 16;
+        std::memcpy(&hf[i], &u, 4);
+      }
+      HIPCHK(hipMemcpy(arena + cj.dst, hf.data(), hf.size() * 4, hipMemcpyHostToDevice));
+    } else {
+      set_error("mk_load_weights: unsupported copy kind");
+      return MK_ERR_SHAPE;
+    }
+  }
+  // ---- tables
+  std::vector<double> inv((size_t)G.shape.head_dim / 2);
+  for (size_t i = 0; i < inv.size(); ++i)
+    inv[i] = std::pow(G.shape.rope_theta, -2.0 * (double)i / (double)G.shape.head_dim);
+  HIPCHK(hipMemcpy(arena + G.off_invfreq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice));
+  Geom ge = G.geom;
+  ge.inv_freq = (const double*)(arena + G.off_invfreq);
+  HIPCHK(hipMemcpy(arena + G.off_geom, &ge, sizeof ge, hipMemcpyHostToDevice));
+  std::vector<OpDesc> od(G.ops.size());
+  auto bufp = [&](int32_t id) -> uint64_t* {
+    if (id < 0 || G.bufs[id].off < 0) return nullptr;
+    return (uint64_t*)(scratch + G.bufs[id].off);
+  };
+  for (size_t i = 0; i < G.ops.size(); ++i) {
+    const OpInst& o = G.ops[i];
+    OpDesc& d = od[i];
+    std::memset(&d, 0, sizeof d);
+    d.kind = o.kind;
+    d.layer = o.layer;
+    d.K = o.K;
+    d.N = o.N;
+    d.norm_in = o.norm_in;
+    d.ntasks = o.ntasks;
+    d.w = o.w_off >= 0 ? (const uint16_t*)(arena + o.w_off) : nullptr;
+    d.g = o.g_off >= 0 ? (const float*)(arena + o.g_off) : nullptr;
+    d.g2 = o.g2_off >= 0 ? (const float*)(arena + o.g2_off) : nullptr;
+    d.in = bufp(o.in_buf);
+    d.res = bufp(o.res_buf);
+    d.out = bufp(o.out_buf);
+    d.aux = bufp(o.aux_buf);
+    d.aux2 = bufp(o.aux2_buf);
+  }
+  HIPCHK(hipMemcpy(arena + G.off_ops, od.data(), od.size() * sizeof(OpDesc), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(arena + G.off_tasks, G.tasks.data(), G.tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
+  if (!G.events.empty())
+    HIPCHK(hipMemcpy(arena + G.off_events, G.events.data(), G.events.size() * sizeof(Event), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(arena + G.off_wloff, G.wl_off.data(), G.wl_off.size() * 4, hipMemcpyHostToDevice));
+  if (!G.wl_ids.empty())
+    HIPCHK(hipMemcpy(arena + G.off_wlids, G.wl_ids.data(), G.wl_ids.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(hipMemsetAsync(scratch, 0, (size_t)G.scratch_bytes, stream));
+  if (G.trace_bytes > 0) HIPCHK(hipMemsetAsync(d_trace, 0, (size_t)G.trace_bytes, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  int wcr = 0;
+  HIPCHK(hipDeviceGetAttribute(&wcr, hipDeviceAttributeWallClockRate, dev));
+  const int64_t us = G.opts.spin_timeout_us > 0 ? G.opts.spin_timeout_us : 2000000;
+  g->budget_ticks = (uint64_t)us * (uint64_t)(wcr > 0 ? wcr : 100000) / 1000ull;
+  for (int nb = 1; nb <= 4; ++nb) {
+    (void)hipFuncSetAttribute(worker_fn(nb), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    (void)hipFuncSetAttribute(lpt_fn(nb), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  }
+  (void)hipGetLastError();
+  g->arena = d_arena;
+  g->scratch = d_scratch;
+  g->trace = d_trace;
+  g->loaded = true;
+  g->epoch = 0;
+  g->tag = 1;
+  return MK_OK;
+}
+
+mk_status mk_set_mode(mk_graph* g, int32_t mode, int32_t per_task_launch) {
+  if (!g || (mode != MK_PERSISTENT && mode != MK_LAUNCH_PER_TASK)) {
+    set_error("mk_set_mode: bad argument");
+    return MK_ERR_ARG;
+  }
+  g->mode = mode;
+  g->per_task_launch = per_task_launch;
+  return MK_OK;
+}
+
+mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
+                         float* d_logits, void* stream_) {
+  if (!g || !g->G) {
+    set_error("mk_decode_step: null graph");
+    return MK_ERR_ARG;
+  }
+  if (!g->loaded) {
+    set_error("mk_decode_step: weights not loaded");
+    return MK_ERR_STATE;
+  }
+  if (!d_tokens || !d_positions || !kv || !kv->k || !kv->v || !d_logits) {
+    set_error("mk_decode_step: null argument");
+    return MK_ERR_ARG;
+  }
+  Graph& G = *g->G;
+  if (kv->capacity != G.cap) {
+    set_error("mk_decode_step: kv capacity " + std::to_string(kv->capacity) + " differs from the graph's max_ctx " +
+              std::to_string(G.cap));
+    return MK_ERR_ARG;
+  }
+  hipStream_t stream = (hipStream_t)stream_;
+  char* arena = (char*)g->arena;
+  char* scratch = (char*)g->scratch;
+  StepArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.geom = (const Geom*)(arena + G.off_geom);
+  a.ops = (const OpDesc*)(arena + G.off_ops);
+  a.tasks = (const Task*)(arena + G.off_tasks);
+  a.events = (const Event*)(arena + G.off_events);
+  a.wl_off = (const int32_t*)(arena + G.off_wloff);
+  a.wl_ids = (const int32_t*)(arena + G.off_wlids);
+  a.counters = (u32*)(scratch + G.off_counters);
+  a.status = (u32*)(scratch + G.off_status);
+  a.tokens = d_tokens;
+  a.positions = d_positions;
+  a.kv_k = (uint16_t*)kv->k;
+  a.kv_v = (uint16_t*)kv->v;
+  a.logits = d_logits;
+  a.trace = (mk_trace_rec*)g->trace;
+  a.budget = g->budget_ticks;
+  a.epoch = g->epoch;
+  a.tag = g->tag;
+  a.magic = G.geom.magic;
+  a.trace_on = G.opts.trace ? 1 : 0;
+  a.n_workers = G.W;
+  const int nb = G.B;
+  if (a.trace_on) HIPCHK(hipMemsetAsync(a.status + ST_TICKET, 0, 2 * sizeof(u32), stream));
+  if (g->mode == MK_PERSISTENT) {
+    hipStream_t side = (hipStream_t)g->side_stream;
+    HIPCHK(hipEventRecord((hipEvent_t)g->ev_a, stream));
+    HIPCHK(hipStreamWaitEvent(side, (hipEvent_t)g->ev_a, 0));
+    hipLaunchKernelGGL(mk_dispatch, dim3(1), dim3(64), 0, side, a);
+    HIPCHK(hipGetLastError());
+    HIPCHK(hipEventRecord((hipEvent_t)g->ev_b, side));
+    void* kargs[] = {&a};
+    hipError_t e = hipLaunchCooperativeKernel(worker_fn(nb), dim3(G.W), dim3(NT), kargs, kLdsBytes, stream);
+    if (e == hipErrorCooperativeLaunchTooLarge) {
+      (void)hipGetLastError();
+      HIPCHK(hipStreamWaitEvent(stream, (hipEvent_t)g->ev_b, 0));
+      set_error("mk_decode_step: " + std::to_string(G.W) + " workers cannot be co-resident on this device");
+      return MK_ERR_NOT_RESIDENT;
+    }
+    if (e != hipSuccess) {
+      set_error(std::string("mk_decode_step: cooperative launch failed: ") + hipGetErrorString(e));
+      return MK_ERR_HIP;
+    }
+    HIPCHK(hipStreamWaitEvent(stream, (hipEvent_t)g->ev_b, 0));
+  } else {
+    const void* fn = lpt_fn(nb);
+    for (size_t i = 0; i < G.launch_first.size(); ++i) {
+      const int32_t first = G.launch_first[i], count = G.launch_count[i];
+      if (g->per_task_launch) {
+        for (int32_t k = 0; k < count; ++k) {
+          a.lpt_first = first + k;
+          void* kargs[] = {&a};
+          HIPCHK(hipLaunchKernel(fn, dim3(1), dim3(NT), kargs, kLdsBytes, stream));
+        }
+      } else {
+        a.lpt_first = first;
+        void* kargs[] = {&a};
+        HIPCHK(hipLaunchKernel(fn, dim3(count), dim3(NT), kargs, kLdsBytes, stream));
+      }
+    }
+  }
+  g->epoch += 1;
+  g->tag += 1;
+  if (g->tag == 0) g->tag = 1;
+  return MK_OK;
+}
+
+mk_status mk_check(mk_graph* g) {
+  if (!g || !g->G || !g->loaded) {
+    set_error("mk_check: graph not loaded");
+    return MK_ERR_STATE;
+  }
+  Graph& G = *g->G;
+  u32 st[ST_WORDS];
+  HIPCHK(hipMemcpy(st, (char*)g->scratch + G.off_status, sizeof st, hipMemcpyDeviceToHost));
+  if (st[ST_ERROR] == ERR_NONE) return MK_OK;
+  std::string msg;
+  mk_status rc = MK_ERR_TIMEOUT;
+  if (st[ST_ERROR] == ERR_TIMEOUT) {
+    int32_t task = (int32_t)st[ST_TASK];
+    msg = "device wait timed out";
+    if (task >= 0 && task < (int32_t)G.tasks.size()) {
+      const Task& t = G.tasks[task];
+      msg += ": task " + std::to_string(task) + " (" + op_kind_name(G.ops[t.op].kind) + ", layer " +
+             std::to_string(G.ops[t.op].layer) + ") waiting on event " + std::to_string((int32_t)st[ST_EVENT]) +
+             " saw " + std::to_string(st[ST_SEEN]) + " of " + std::to_string(st[ST_TARGET]);
+    } else if (task == -1) {
+      msg += ": the dispatcher saw " + std::to_string(st[ST_SEEN]) + " of " + std::to_string(st[ST_TARGET]) +
+             " workers finish";
+    } else {
+      msg += ": an activation word kept a stale tag";
+    }
+  } else if (st[ST_ERROR] == ERR_CONFIG) {
+    msg = "device tables do not match the graph (reload the weights)";
+    rc = MK_ERR_STATE;
+  } else if (st[ST_ERROR] == ERR_BAD_INPUT) {
+    msg = "token id or position out of range";
+    rc = MK_ERR_ARG;
+  } else {
+    msg = "device error " + std::to_string(st[ST_ERROR]);
+    rc = MK_ERR_STATE;
+  }
+  // reset the event state so that the next step can run
+  HIPCHK(hipMemset((char*)g->scratch + G.off_counters, 0, (size_t)(G.off_status - G.off_counters) + ST_WORDS * 4));
+  HIPCHK(hipDeviceSynchronize());
+  g->epoch = 0;
+  set_error("mk_check: " + msg);
+  return rc;
+}
+
+mk_status mk_read_trace(mk_graph* g, mk_trace_rec* host_buf, int64_t cap, int64_t* n) {
+  if (!g || !g->G || !g->loaded || !n) {
+    set_error("mk_read_trace: bad argument");
+    return MK_ERR_ARG;
+  }
+  Graph& G = *g->G;
+  if (!g->trace) {
+    set_error("mk_read_trace: graph built without trace");
+    return MK_ERR_STATE;
+  }
+  u32 cnt = 0;
+  HIPCHK(hipMemcpy(&cnt, (char*)g->scratch + G.off_status + ST_TRACE_N * 4, 4, hipMemcpyDeviceToHost));
+  int64_t m = std::min<int64_t>({(int64_t)cnt, cap, (int64_t)G.tasks.size()});
+  if (m > 0 && host_buf) HIPCHK(hipMemcpy(host_buf, g->trace, (size_t)m * sizeof(mk_trace_rec), hipMemcpyDeviceToHost));
+  *n = (int64_t)cnt;
+  return MK_OK;
+}
+
+mk_status mk_read_counters(mk_graph* g, uint32_t* host_counters, int64_t cap) {
+  if (!g || !g->G || !g->loaded || !host_counters) {
+    set_error("mk_read_counters: bad argument");
+    return MK_ERR_ARG;
+  }
+  Graph& G = *g->G;
+  const int64_t ne = (int64_t)G.events.size();
+  if (cap < ne) {
+    set_error("mk_read_counters: buffer too small");
+    return MK_ERR_ARG;
+  }
+  std::vector<u32> raw((size_t)ne * kSubCounters * kCounterStride);
+  if (ne > 0) HIPCHK(hipMemcpy(raw.data(), (char*)g->scratch + G.off_counters, raw.size() * 4, hipMemcpyDeviceToHost));
+  for (int64_t e = 0; e < ne; ++e) {
+    u32 s = 0;
+    for (int k = 0; k < kSubCounters; ++k) s += raw[((size_t)e * kSubCounters + k) * kCounterStride];
+    host_counters[e] = s;
+  }
+  return MK_OK;
+}
+
+mk_status mk_graph_stats(const mk_graph* g, mk_stats* out) {
+  if (!g || !g->G || !out) {
+    set_error("mk_graph_stats: null argument");
+    return MK_ERR_ARG;
+  }
+  const Graph& G = *g->G;
+  std::memset(out, 0, sizeof *out);
+  out->tasks = (int64_t)G.tasks.size();
+  out->empty_tasks = G.n_empty;
+  out->events = (int64_t)G.events.size();
+  out->ops = (int64_t)G.ops.size();
+  out->workers = G.W;
+  out->launches_per_step = (int64_t)G.launch_first.size();
+  out->raw_edges = (int64_t)G.raw_edges.size();
+  out->reduced_edges = G.n_reduced_edges;
+  for (int32_t w = 0; w < G.W; ++w)
+    out->max_tasks_per_worker = std::max<int64_t>(out->max_tasks_per_worker, G.wl_off[w + 1] - G.wl_off[w]);
+  out->weight_bytes = G.weight_bytes_step;
+  out->arena_bytes = G.arena_bytes;
+  out->scratch_bytes = G.scratch_bytes;
+  out->trace_bytes = G.trace_bytes;
+  out->batch = G.B;
+  out->max_ctx = G.cap;
+  out->attn_chunks = G.C;
+  out->gemv = G.gemv;
+  return MK_OK;
+}
+
+mk_status mk_dump_graph(const mk_graph* g, const char* json_path) {
+  if (!g || !g->G || !json_path) {
+    set_error("mk_dump_graph: null argument");
+    return MK_ERR_ARG;
+  }
+  dump_json(*g->G, json_path);
+  return MK_OK;
+}
+
+mk_status mk_get_tasks(const mk_graph* g, int32_t* rows, int64_t cap) {
+  if (!g || !g->G || !rows || cap < (int64_t)g->G->tasks.size()) {
+    set_error("mk_get_tasks: bad argument");
+    return MK_ERR_ARG;
+  }
+  const Graph& G = *g->G;
+  for (size_t i = 0; i < G.tasks.size(); ++i) {
+    const Task& t = G.tasks[i];
+    int32_t* r = rows + 8 * i;
+    r[0] = G.ops[t.op].kind;
+    r[1] = G.ops[t.op].layer;
+    r[2] = t.dep;
+    r[3] = t.trig;
+    r[4] = t.a0;
+    r[5] = t.a1;
+    r[6] = t.a2;
+    r[7] = t.a3;
+  }
+  return MK_OK;
+}
+
+mk_status mk_get_events(const mk_graph* g, int32_t* rows, int64_t cap) {
+  if (!g || !g->G || !rows || cap < (int64_t)g->G->events.size()) {
+    set_error("mk_get_events: bad argument");
+    return MK_ERR_ARG;
+  }
+  const Graph& G = *g->G;
+  for (size_t i = 0; i < G.events.size(); ++i) {
+    rows[4 * i] = G.events[i].need;
+    rows[4 * i + 1] = G.events[i].first;
+    rows[4 * i + 2] = G.events[i].last;
+    rows[4 * i + 3] = G.events[i].producers;
+  }
+  return MK_OK;
+}
+
+mk_status mk_get_worker_lists(const mk_graph* g, int32_t* offsets, int32_t* ids, int64_t cap) {
+  if (!g || !g->G || !offsets || !ids || cap < (int64_t)g->G->wl_ids.size()) {
+    set_error("mk_get_worker_lists: bad argument");
+    return MK_ERR_ARG;
+  }
+  const Graph& G = *g->G;
+  std::memcpy(offsets, G.wl_off.data(), G.wl_off.size() * 4);
+  std::memcpy(ids, G.wl_ids.data(), G.wl_ids.size() * 4);
+  return MK_OK;
+}
+
+mk_status mk_get_raw_edges(const mk_graph* g, int32_t* rows, int64_t cap, int64_t* n) {
+  if (!g || !g->G || !n) {
+    set_error("mk_get_raw_edges: bad argument");
+    return MK_ERR_ARG;
+  }
+  const Graph& G = *g->G;
+  *n = (int64_t)G.raw_edges.size();
+  if (!rows) return MK_OK;
+  if (cap < *n) {
+    set_error("mk_get_raw_edges: buffer too small");
+    return MK_ERR_ARG;
+  }
+  for (size_t i = 0; i < G.raw_edges.size(); ++i) {
+    rows[2 * i] = G.raw_edges[i].first;
+    rows[2 * i + 1] = G.raw_edges[i].second;
+  }
+  return MK_OK;
+}
+
+void mk_destroy_graph(mk_graph* g) {
+  if (!g) return;
+  if (g->side_stream) (void)hipStreamDestroy((hipStream_t)g->side_stream);
+  if (g->ev_a) (void)hipEventDestroy((hipEvent_t)g->ev_a);
+  if (g->ev_b) (void)hipEventDestroy((hipEvent_t)g->ev_b);
+  delete g->G;
+  delete g;
+}
+
+const char* mk_hip_runtime_path(void) {
+  static std::string path;
+  Dl_info info;
+  if (dladdr((void*)&hipGetDeviceCount, &info) && info.dli_fname) path = info.dli_fname;
+  return path.c_str();
+}
+
+}  // extern "C"

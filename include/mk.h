@@ -1,0 +1,234 @@
+/*
+ * mk.h - C ABI of the persistent decode megakernel for MI355X (gfx950).
+ *
+ * One call of mk_decode_step runs one autoregressive decode step of a
+ * Qwen3-style decoder (dense SwiGLU MLP, or top-k routed experts) for a batch
+ * of sequences, either
+ *   - PERSISTENT: one launch of a worker kernel with one workgroup resident on
+ *     every compute unit plus a one-wavefront dispatch kernel on a second
+ *     stream; workers run their statically assigned task lists and wait only on
+ *     atomic event counters (MPK page "Mirage Persistent Kernel (MPK)", sections
+ *     3.2 and 5.1: one compute kernel launched with one block per worker plus a
+ *     dispatch-only scheduler kernel on its own stream), or
+ *   - LAUNCH_PER_TASK: the same task bodies, one kernel launch per operator
+ *     range in the same order, stream order replacing the events (the
+ *     kernel-per-operator baseline of the same pages, section 3.2, and of the
+ *     Spheron article "Compile a Megakernel With Mirage", section
+ *     "Kernel-Per-Operator Dispatch").
+ *
+ * The task graph comes from a host compiler (mk_build_graph): every operator
+ * is tiled into CU-sized tasks, events are fused and normalised so that each
+ * task waits on at most one event and triggers at most one, and the graph is
+ * BFS-linearised so that each event's dependents are one contiguous task range
+ * (MPK review page 2512.22219, section 2.4; MPK abstract: an SM-level task
+ * graph executed with decentralised in-kernel scheduling).
+ *
+ * Conventions
+ *  - Every device pointer is memory the CALLER allocated and owns (PyTorch in
+ *    the bundled binding).  The library never allocates or frees device memory;
+ *    it owns only the host-side mk_graph and one internal HIP stream.
+ *  - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16), row-major
+ *    [out, in] as in a linear layer.
+ *  - Calls that take a stream enqueue asynchronous work on it; results are
+ *    valid after the caller synchronises that stream.  Argument and shape
+ *    errors are reported synchronously and nothing is enqueued.
+ *  - Every call returns MK_OK (0) or a negative mk_status; mk_last_error()
+ *    gives a message for the calling thread's last failure.  No C++ exception
+ *    crosses this boundary.
+ *  - One mk_graph must not be used from two host threads at once, and steps
+ *    of one graph must be issued in order on one stream.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mk_status;
+#define MK_OK 0
+#define MK_ERR_ARG (-1)          /* bad argument (null pointer, out-of-range value) */
+#define MK_ERR_SHAPE (-2)        /* shapes inconsistent or unsupported */
+#define MK_ERR_HIP (-3)          /* a HIP runtime call failed */
+#define MK_ERR_NOT_RESIDENT (-4) /* workers could not all be co-resident */
+#define MK_ERR_TIMEOUT (-5)      /* a device wait exceeded its time budget (watchdog) */
+#define MK_ERR_TRACE (-6)        /* the task trace violates the graph */
+#define MK_ERR_STATE (-7)        /* call out of order (e.g. decode before load) */
+
+typedef struct mk_graph mk_graph;
+
+/* Model shape.  Dense models set n_experts = 0; routed models set
+ * n_experts/top_k/expert_intermediate and leave intermediate = 0.
+ * head_dim must be a multiple of 64 and at most 128; n_q_heads must be a
+ * multiple of n_kv_heads. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate;
+  int32_t n_experts, top_k, expert_intermediate, vocab, tied_embeddings;
+  float rms_eps;     /* RMSNorm epsilon (1e-6) */
+  double rope_theta; /* RoPE base (1e6) */
+} mk_model_shape;
+
+#define MK_PERSISTENT 0
+#define MK_LAUNCH_PER_TASK 1
+
+#define MK_GEMV_AUTO 0 /* VALU dot products below batch 8, MFMA from batch 8 */
+#define MK_GEMV_VALU 1
+#define MK_GEMV_MFMA 2
+
+typedef struct {
+  int32_t mode;            /* MK_PERSISTENT or MK_LAUNCH_PER_TASK (mk_set_mode can switch) */
+  int32_t per_task_launch; /* launch-per-task only: 1 = one launch per task (stress mode) */
+  int32_t num_workers;     /* 0 = the device's compute-unit count */
+  int32_t trace;           /* 1 = record one mk_trace_rec per executed task */
+  int32_t attn_chunks;     /* attention chunks per (sequence, kv head); 0 = auto */
+  int32_t gemv;            /* MK_GEMV_* */
+  int32_t spin_timeout_us; /* watchdog budget of any single device wait; 0 = 2 s */
+  int32_t no_fusion;       /* 1 = one event per dependency edge (analysis only: normalisation then
+                              inserts empty tasks); 0 = fuse events (default) */
+  int32_t reserved[8];     /* must be zero */
+} mk_build_opts;
+
+/* One logical tensor handed to mk_load_weights.  Names:
+ *   embed [V,H], final_norm [H], lm_head [V,H] (absent when tied),
+ *   layers.{l}.{in_norm [H], wq [Hq*D,H], wk [Hkv*D,H], wv [Hkv*D,H],
+ *               q_norm [D], k_norm [D], wo [H,Hq*D], post_norm [H]}
+ *   dense:  layers.{l}.{w_gate [I,H], w_up [I,H], w_down [H,I]}
+ *   routed: layers.{l}.router [E,H], layers.{l}.experts.{e}.{w_gate,w_up [Ie,H], w_down [H,Ie]}
+ * Vectors use cols = 1.  data is bf16; on_device = 1 if data is device memory. */
+typedef struct {
+  const char* name;
+  const void* data;
+  int64_t rows, cols;
+  int32_t on_device;
+} mk_tensor;
+
+/* Contiguous bf16 KV cache, each of k and v laid out [L][B][Hkv][capacity][D].
+ * positions[b] of a step is the slot that step writes; attention covers slots
+ * 0..positions[b] of sequence b.  capacity must equal the graph's max_ctx. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t capacity;
+} mk_kv_cache;
+
+/* One record per executed task (trace mode).  Tickets come from one global
+ * atomic counter: start is taken after the task's dependency wait succeeded,
+ * end is taken before its trigger. */
+typedef struct {
+  int32_t task;     /* task id (BFS order) */
+  int16_t worker;   /* worker (workgroup) index; -1 in launch-per-task mode */
+  int16_t xcc;      /* hardware XCC (chiplet) id the task ran on */
+  uint32_t t_start; /* global ticket at start */
+  uint32_t t_end;   /* global ticket at end (before the trigger) */
+  uint32_t dep_seen;/* dependency counter value observed when the wait ended */
+  uint32_t step;    /* step epoch */
+  uint32_t clk_start, clk_end; /* low 32 bits of the 100 MHz device wall clock */
+} mk_trace_rec;
+
+typedef struct {
+  int64_t tasks;             /* tasks per step, including empty ones */
+  int64_t empty_tasks;       /* tasks inserted by normalisation */
+  int64_t events;            /* events after fusion and normalisation */
+  int64_t ops;               /* operator instances */
+  int64_t workers;
+  int64_t launches_per_step; /* launch-per-task mode, range granularity */
+  int64_t raw_edges;         /* task dependency edges before reduction */
+  int64_t reduced_edges;     /* after transitive reduction */
+  int64_t max_tasks_per_worker;
+  int64_t weight_bytes;      /* weight bytes one step streams (dense) */
+  int64_t arena_bytes, scratch_bytes, trace_bytes;
+  int32_t batch, max_ctx, attn_chunks, gemv;
+} mk_stats;
+
+/* Compile the task graph for a model shape, batch and KV capacity (host only;
+ * no device work).  *out receives a new graph, freed by mk_destroy_graph.
+ * Errors: MK_ERR_ARG, MK_ERR_SHAPE. */
+mk_status mk_build_graph(const mk_model_shape* shape, int32_t batch, int32_t max_ctx, const mk_build_opts* opts,
+                         mk_graph** out);
+
+/* Bytes of caller-allocated device memory the graph needs:
+ *   arena   - packed weights and the read-only task tables (256 B aligned)
+ *   scratch - event counters, status words and inter-task activations
+ *   trace   - trace records (0 unless opts.trace) */
+mk_status mk_workspace_size(const mk_graph* g, size_t* arena_bytes, size_t* scratch_bytes, size_t* trace_bytes);
+
+/* Repack the logical tensors into the arena in per-task order, upload the
+ * task tables, and clear the scratch.  Asynchronous on `stream` (a
+ * hipStream_t; NULL = default stream); host tensors are staged synchronously.
+ * Every tensor of the shape must be present exactly once.
+ * Errors: MK_ERR_ARG (missing/duplicate/misshapen tensor), MK_ERR_HIP. */
+mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void* d_arena, void* d_scratch,
+                          void* d_trace, void* stream);
+
+/* Run one decode step: tokens d_tokens[B] (int32) at positions d_positions[B]
+ * (int32, 0 <= pos < capacity), reading/writing the KV cache, and writing
+ * fp32 logits d_logits[B][V].  Asynchronous on `stream`.
+ * Errors: MK_ERR_STATE (weights not loaded, or a previous step failed and was
+ * not cleared by mk_check), MK_ERR_ARG, MK_ERR_HIP, MK_ERR_NOT_RESIDENT. */
+mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
+                         float* d_logits, void* stream);
+
+/* Switch the execution mode of a loaded graph (same tables and arena). */
+mk_status mk_set_mode(mk_graph* g, int32_t mode, int32_t per_task_launch);
+
+/* After the caller synchronised the stream: read the device status word.
+ * MK_OK, or MK_ERR_TIMEOUT (watchdog fired; the details are in the message),
+ * after which the event state is reset so that the next step can run. */
+mk_status mk_check(mk_graph* g);
+
+/* After sync: copy the trace of the last step (up to cap records) to host
+ * memory; *n receives the number of records written by the device. */
+mk_status mk_read_trace(mk_graph* g, mk_trace_rec* host_buf, int64_t cap, int64_t* n);
+
+/* After sync: verify a trace against the graph: every task exactly once, no
+ * task started before all triggers of its dependency event ended, observed
+ * counters at or above their targets, and (if counters != NULL, from
+ * mk_read_counters) every event counter equal to need * steps.
+ * MK_OK or MK_ERR_TRACE (first violation in the message). */
+mk_status mk_check_trace(const mk_graph* g, const mk_trace_rec* recs, int64_t n, uint32_t step,
+                         const uint32_t* counters);
+
+/* After sync: host copy of the per-event counter totals (events entries). */
+mk_status mk_read_counters(mk_graph* g, uint32_t* host_counters, int64_t cap);
+
+/* Execute the graph's protocol on the host with `threads` threads standing in
+ * for the workers and no-op task bodies, writing a trace (recs, cap >= tasks)
+ * for mk_check_trace.  `fault` plants a protocol fault for checker tests:
+ * 0 none, 1 drop one trigger (expect MK_ERR_TIMEOUT), 2 duplicate one trigger,
+ * 3 start one task without waiting.  Host only, no device. */
+mk_status mk_simulate(const mk_graph* g, int32_t threads, int32_t steps, int32_t fault, int32_t timeout_ms,
+                      mk_trace_rec* recs, int64_t cap, int64_t* n, uint32_t* counters);
+
+mk_status mk_graph_stats(const mk_graph* g, mk_stats* out);
+
+/* Write the graph (tasks, events, worker lists) as JSON. */
+mk_status mk_dump_graph(const mk_graph* g, const char* json_path);
+
+/* Host copies of the graph tables for inspection and tests.
+ * task rows: {op_kind, layer, dep_event, trig_event, a0, a1, a2, a3} (int32 x 8)
+ * event rows: {need, first, last, producers} (int32 x 4)
+ * worker lists: CSR (offsets[workers+1], ids[tasks]) */
+mk_status mk_get_tasks(const mk_graph* g, int32_t* rows, int64_t cap);
+mk_status mk_get_events(const mk_graph* g, int32_t* rows, int64_t cap);
+mk_status mk_get_worker_lists(const mk_graph* g, int32_t* offsets, int32_t* ids, int64_t cap);
+
+/* Raw dependency edges (producer, consumer) the compiler derived from the
+ * tasks' read/write footprints before any reduction (brute-force check of
+ * edge preservation).  *n receives the count; pass rows = NULL to query. */
+mk_status mk_get_raw_edges(const mk_graph* g, int32_t* rows, int64_t cap, int64_t* n);
+
+void mk_destroy_graph(mk_graph* g);
+const char* mk_last_error(void);
+
+/* Path of the loaded HIP runtime library (diagnostic: it must be the same one
+ * the caller's framework uses). */
+const char* mk_hip_runtime_path(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H */

@@ -1,0 +1,86 @@
+"""End-to-end parity of the HIP decoder against the oracle, through the C ABI.
+
+Every step compares logits (relative L2 <= 1e-2) and greedy tokens (equal when
+the oracle's top-2 margin > 0.05) under teacher forcing, and in trace mode the
+integer task trace of every step is checked against the graph: each task
+exactly once, no task started before the triggers of its dependency event
+ended, observed counters at their targets, final counters = need x steps.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_megakernel_persistent_amd as mk
+import synth
+from tests import harness
+
+pytestmark = pytest.mark.gpu
+
+
+def run_steps(w, prep, mode, steps, trace=True, workers=0, gemv=mk.MK_GEMV_AUTO, attn_chunks=0):
+    opts = mk.make_opts(mode=mode, trace=int(trace), num_workers=workers, gemv=gemv, attn_chunks=attn_chunks)
+    sess = mk.Session(w.shape, w.batch, w.capacity, opts)
+    try:
+        sess.load(prep.weights)
+        sess.set_kv(prep.k0, prep.v0)
+        orc = harness.oracle.Oracle(w.shape, w.batch, w.capacity)
+        orc.set_weights(prep.weights)
+        orc.K[...] = prep.k0
+        orc.V[...] = prep.v0
+        tok, pos = prep.tokens.copy(), prep.positions.copy()
+        reports = []
+        for s in range(steps):
+            harness.log(f"[step] {w.name} mode={mode} step={s} pos={pos.tolist()[:4]}")
+            lg_g = sess.step(tok, pos)
+            torch.cuda.synchronize()
+            sess.check()
+            lg_g = lg_g.cpu().numpy()
+            lg_o = orc.decode(tok, pos)
+            rep = harness.compare(lg_g, lg_o)
+            reports.append(rep)
+            if trace:
+                recs = sess.read_trace()
+                cnt = sess.read_counters()
+                sess.check_trace(recs, s, cnt)
+            tok = harness.oracle.greedy(lg_o)
+            pos = pos + 1
+        return reports, sess.stats
+    finally:
+        sess.close()
+
+
+def assert_reports(reports):
+    worst = max(r["rel_l2"] for rep in reports for r in rep)
+    bad = [(s, b, r) for s, rep in enumerate(reports) for b, r in enumerate(rep) if not r["ok"]]
+    harness.log(f"[parity] steps={len(reports)} worst rel_l2={worst:.3e} failures={len(bad)}")
+    assert not bad, f"parity failures (step, seq, report): {bad[:5]}"
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.WORKLOADS["tiny"]
+    return w, harness.prepare(w)
+
+
+@pytest.mark.parametrize("mode", [mk.MK_PERSISTENT, mk.MK_LAUNCH_PER_TASK])
+def test_tiny_16_steps(tiny, mode):
+    w, prep = tiny
+    reports, _ = run_steps(w, prep, mode, steps=w.steps)
+    assert_reports(reports)
+
+
+def test_tiny_small_worker_count(tiny):
+    # fewer workers than tasks per op: several tasks of one op per worker
+    w, prep = tiny
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=3, workers=8)
+    assert st.workers == 8
+    assert_reports(reports)
+
+
+def test_tiny_one_chunk_and_many_chunks(tiny):
+    w, prep = tiny
+    for C in (1, 7):
+        reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=2, attn_chunks=C)
+        assert st.attn_chunks == C
+        assert_reports(reports)
