@@ -42,6 +42,7 @@ struct StepArgs {
   const int32_t* wl_ids;
   u32* counters;
   u32* status;
+  u32* progress;   // per agent: 1 + id of the current task, 0xFFFFFFFF when done
   const int32_t* tokens;
   const int32_t* positions;
   uint16_t* kv_k;
@@ -69,16 +70,30 @@ DEV uint16_t f2bf(float f) {
 }
 DEV float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// ---------------------------------------------------------------- global pointers
+// Table entries hold generic pointers; casting them to the global address
+// space makes the compiler emit global_* instead of flat_* memory operations
+// (flat operations also occupy the LDS/scalar wait counter).
+typedef __attribute__((address_space(1))) u64 g_u64;
+typedef __attribute__((address_space(1))) u32 g_u32;
+DEV g_u64* gp(u64* p) { return (g_u64*)p; }
+DEV const g_u64* gp(const u64* p) { return (const g_u64*)p; }
+DEV g_u32* gp(u32* p) { return (g_u32*)p; }
+typedef __attribute__((address_space(1))) const float g_cf32;
+DEV float ldg(const float* p) { return *(g_cf32*)p; }
+
 // ---------------------------------------------------------------- tagged words
 DEV u64 pack(float v, u32 tag) { return ((u64)tag << 32) | (u64)__float_as_uint(v); }
 DEV void st_t(u64* p, float v, u32 tag) {
-  __hip_atomic_store(p, pack(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), pack(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Slow path of a tagged read: re-read at agent scope until the word carries
+// this step's tag (agent-scope loads observe other XCDs' agent-scope stores).
 __device__ __noinline__ u64 ld_t_slow(const u64* p, u32 tag, u64 budget, u32* status) {
   const u64 t0 = wall_clock64();
   for (int i = 0;; ++i) {
-    u64 w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    u64 w = __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((u32)(w >> 32) == tag) return w;
     if ((i & 7) == 7) {
       if (__hip_atomic_load(status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
@@ -90,6 +105,8 @@ __device__ __noinline__ u64 ld_t_slow(const u64* p, u32 tag, u64 budget, u32* st
           __hip_atomic_store(status + ST_SEEN, (u32)(w >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(status + ST_TARGET, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        __hip_atomic_store(status + ST_ADDR_LO, (u32)(uintptr_t)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(status + ST_ADDR_HI, (u32)((uintptr_t)p >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(status + ST_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return pack(0.0f, tag);
       }
@@ -99,12 +116,15 @@ __device__ __noinline__ u64 ld_t_slow(const u64* p, u32 tag, u64 budget, u32* st
 }
 
 // Fast path: a workgroup-scope relaxed load (a plain cached load: one fetch
-// per XCD, shared through its L2); fall back when the tag is stale.
-DEV float ld_t(const u64* p, const StepArgs& a) {
-  u64 w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// per XCD, shared through its L2); fall back when the tag is stale.  Callers
+// that read several words issue every ld_raw first and check the tags after,
+// so a batch costs one memory round trip.
+DEV u64 ld_raw(const u64* p) { return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
+DEV float fix_t(u64 w, const u64* p, const StepArgs& a) {
   if ((u32)(w >> 32) != a.tag) w = ld_t_slow(p, a.tag, a.budget, a.status);
   return __uint_as_float((u32)w);
 }
+DEV float ld_t(const u64* p, const StepArgs& a) { return fix_t(ld_raw(p), p, a); }
 
 // ---------------------------------------------------------------- reductions
 DEV float dpp_f(float v, int ctrl);
@@ -118,6 +138,13 @@ DEV float row16_sum(float v) {
   v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp<0x124>(v);  // row_ror:4
   v += dpp<0x128>(v);  // row_ror:8
+  return v;
+}
+// Sum over each 8-lane half row (result in every lane of the half row).
+DEV float row8_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
   return v;
 }
 DEV float row16_max(float v) {
@@ -152,7 +179,7 @@ struct Ctx {
 DEV u32 event_total(const StepArgs& a, int ev, int lane) {
   u32 v = 0;
   if (lane < kSubCounters)
-    v = __hip_atomic_load(a.counters + ((size_t)ev * kSubCounters + lane) * kCounterStride, __ATOMIC_RELAXED,
+    v = __hip_atomic_load(gp(a.counters + ((size_t)ev * kSubCounters + lane) * kCounterStride), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
   v += __shfl_xor(v, 1);
   v += __shfl_xor(v, 2);
@@ -169,6 +196,8 @@ DEV void report_timeout(const StepArgs& a, int task, int ev, u32 seen, u32 targe
     __hip_atomic_store(a.status + ST_SEEN, seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(a.status + ST_TARGET, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // the most upstream (smallest id) task that timed out
+  if (task >= 0) __hip_atomic_fetch_min(a.status + ST_MIN_TASK, (u32)task, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(a.status + ST_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -213,11 +242,12 @@ DEV void wait_dep(Ctx& c) {
   __syncthreads();
 }
 
-// All threads: make this thread's stores complete, then one thread records
-// the trace and triggers the task's event.
+// All threads: once every thread has issued its output stores, one thread
+// records the trace and triggers the task's event.  The trigger does not wait
+// for the stores to be acknowledged: a consumer that reads a word before it
+// lands sees the old tag and re-reads it.
 DEV void finish(Ctx& c) {
   const StepArgs& a = *c.a;
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are acknowledged
   __syncthreads();
   if (threadIdx.x == 0) {
     if (a.trace_on && !c.flags[0]) {
@@ -239,7 +269,7 @@ DEV void finish(Ctx& c) {
     }
     if (c.t.trig >= 0 && !c.flags[0]) {
       const int sub = (c.agent >= 0 ? c.agent : (int)blockIdx.x) & (kSubCounters - 1);
-      __hip_atomic_fetch_add(a.counters + ((size_t)c.t.trig * kSubCounters + sub) * kCounterStride, 1u,
+      __hip_atomic_fetch_add(gp(a.counters + ((size_t)c.t.trig * kSubCounters + sub) * kCounterStride), 1u,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -288,32 +318,65 @@ DEV void body_embed(Ctx& c, const OpDesc& op) {
 template <int NB>
 DEV void stage_input(Ctx& c, const OpDesc& op, float* xs, float* red) {
   const StepArgs& a = *c.a;
-  const int K = op.K;
+  const int K = op.K, tid = threadIdx.x;
+  constexpr int CH = 8;  // tagged words in flight per thread
+  const bool nrm = op.norm_in != 0;
   float ss[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     ss[b] = 0.f;
     const u64* in = op.in + (size_t)b * K;
-    for (int k = threadIdx.x; k < K; k += NT) {
-      float v = ld_t(in + k, a);
-      xs[b * K + k] = v;
-      ss[b] += v * v;
+    for (int k0 = 0; k0 < K; k0 += NT * CH) {
+      u64 w[CH];
+      float gv[CH];
+      // unconditional loads (clamped index) so that all of them are in
+      // flight before the first tag check
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int k = min(k0 + tid + i * NT, K - 1);
+        w[i] = ld_raw(in + k);
+      }
+      if (nrm) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) gv[i] = ldg(op.g + min(k0 + tid + i * NT, K - 1));
+      } else {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) gv[i] = 1.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int k = k0 + tid + i * NT;
+        if (k < K) {
+          const float v = fix_t(w[i], in + k, a);
+          xs[b * K + k] = v * gv[i];
+          ss[b] += v * v;
+        }
+      }
     }
   }
-  if (op.norm_in) {
+  if (nrm) {
     block_sum<NB>(ss, red);
     const float eps = a.geom->eps;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const float r = rsqrtf(ss[b] / (float)K + eps);
-      for (int k = threadIdx.x; k < K; k += NT) xs[b * K + k] = xs[b * K + k] * r * op.g[k];
+      for (int k = tid; k < K; k += NT) xs[b * K + k] *= r;
     }
   }
 }
 
 // ---------------------------------------------------------------- GEMV epilogue
+// Residual words of this thread's first epilogue output, loaded right after
+// the wait so that the load overlaps the weight stream.
+DEV u64 gemv_residual_prefetch(const Ctx& c, const OpDesc& op, int NB) {
+  const int nr = c.t.a2, j = threadIdx.x;
+  if ((op.kind != OP_OPROJ && op.kind != OP_DOWN) || j >= NB * nr) return 0ull;
+  const int b = j / nr, row = c.t.a1 + (j - b * nr);
+  return ld_raw(op.res + (size_t)b * op.N + row);
+}
+
 template <int NB>
-DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR) {
+DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 res0) {
   const StepArgs& a = *c.a;
   const int nr = c.t.a2, r0 = c.t.a1, N = op.N;
   for (int j = threadIdx.x; j < NB * nr; j += NT) {
@@ -325,9 +388,12 @@ DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR) {
         st_t(op.out + (size_t)b * N + row, v, a.tag);
         break;
       case OP_OPROJ:
-      case OP_DOWN:
-        st_t(op.out + (size_t)b * N + row, ld_t(op.res + (size_t)b * N + row, a) + v, a.tag);
+      case OP_DOWN: {
+        const u64* rp = op.res + (size_t)b * N + row;
+        const float rv = j == (int)threadIdx.x ? fix_t(res0, rp, a) : ld_t(rp, a);
+        st_t(op.out + (size_t)b * N + row, rv + v, a.tag);
         break;
+      }
       case OP_GATEUP:
         st_t(op.out + (size_t)b * N + row, silu(v) * rsl[b * NR + nr + r], a.tag);
         break;
@@ -349,7 +415,9 @@ DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR) {
 // resource so out-of-range segments return zeros without touching memory.
 template <int NB, int S>
 DEV void gemv_valu(Ctx& c, const OpDesc& op) {
-  constexpr int DEPTH = S >= 8 ? 4 : S >= 6 ? 5 : S >= 4 ? 8 : S >= 3 ? 10 : S >= 2 ? 16 : 32;
+  // about 28 loads in flight per lane (24 when 3-4 sequences need more accumulators)
+  constexpr int LOADS = NB <= 2 ? 28 : 24;
+  constexpr int DEPTH = LOADS / S > 1 ? LOADS / S : 2;
   const Task& t = c.t;
   const int K = op.K, CPR = K >> 3, NCH = (CPR + 63) >> 6, SPR = NCH / S;
   const bool gu = op.kind == OP_GATEUP;
@@ -380,6 +448,7 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   float* xs = (float*)c.lds;
   float* rsl = xs + kStageFloats;
   float* red = (float*)(c.flags + 8);
+  const u64 res0 = gemv_residual_prefetch(c, op, NB);
   stage_input<NB>(c, op, xs, red);
   __syncthreads();
 
@@ -430,19 +499,20 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
     }
   }
   __syncthreads();
-  gemv_epilogue<NB>(c, op, rsl, NR);
+  gemv_epilogue<NB>(c, op, rsl, NR, res0);
 }
 
 template <int NB>
 DEV void gemv_valu_any(Ctx& c, const OpDesc& op) {
   const int nch = ((op.K >> 3) + 63) >> 6;
-  if (nch % 8 == 0) gemv_valu<NB, 8>(c, op);
+  if (nch % 4 == 0) gemv_valu<NB, 4>(c, op);
   else if (nch % 6 == 0) gemv_valu<NB, 6>(c, op);
-  else if (nch % 4 == 0) gemv_valu<NB, 4>(c, op);
   else if (nch % 3 == 0) gemv_valu<NB, 3>(c, op);
   else if (nch % 2 == 0) gemv_valu<NB, 2>(c, op);
   else gemv_valu<NB, 1>(c, op);
 }
+
+DEV void merge_partials(Ctx& c, const u64* parts, u64* out, int b, int g);
 
 // ---------------------------------------------------------------- attention
 // One (sequence b, kv head g, chunk) task: q-norm + RoPE for the G query
@@ -490,6 +560,18 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
     vr[p] = __builtin_amdgcn_raw_buffer_load_b128(rv, roff(p), 0, AUX_NT);
   }
 
+  // inputs that do not depend on this step: gains and RoPE frequencies
+  const int half = D >> 1;
+  float gq0 = 0.f, gq1 = 0.f, gk0 = 0.f, gk1 = 0.f;
+  double ifreq = 0.0;
+  if (lane < half) {
+    gq0 = ldg(op.g + lane);
+    gq1 = ldg(op.g + lane + half);
+    gk0 = ldg(op.g2 + lane);
+    gk1 = ldg(op.g2 + lane + half);
+    ifreq = G.inv_freq[lane];
+  }
+
   wait_dep(c);
 
   float* qs = (float*)c.lds;                 // [NG][D], pre-scaled by 1/sqrt(D)
@@ -502,13 +584,16 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
 
   // q / k / v prologue: wavefront h handles head h (then k at NG, v at NG+1)
   const u64* qkv = op.in + (size_t)b * G.qkv_stride + (size_t)g * (NG + 2) * D;
-  const int half = D >> 1;
   for (int h = wave; h < NG + 2; h += NWAVE) {
     if (h >= NG && !last) continue;
     float x0 = 0.f, x1 = 0.f;
-    if (lane < half) {
-      x0 = ld_t(qkv + (size_t)h * D + lane, a);
-      x1 = ld_t(qkv + (size_t)h * D + lane + half, a);
+    {
+      const u64* p0 = qkv + (size_t)h * D + (lane < half ? lane : 0);
+      const u64 w0 = ld_raw(p0), w1 = ld_raw(p0 + half);
+      if (lane < half) {
+        x0 = fix_t(w0, p0, a);
+        x1 = fix_t(w1, p0 + half, a);
+      }
     }
     if (h == NG + 1) {
       if (lane < half) {
@@ -523,12 +608,14 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
     const float ss = wave_sum(x0 * x0 + x1 * x1);
     const float r = rsqrtf(ss / (float)D + G.eps);
     if (lane < half) {
-      const float* gain = h < NG ? op.g : op.g2;
-      x0 *= r * gain[lane];
-      x1 *= r * gain[lane + half];
-      double sn, cs;
-      sincos((double)pos * G.inv_freq[lane], &sn, &cs);
-      const float cf = (float)cs, sf = (float)sn;
+      x0 *= r * (h < NG ? gq0 : gk0);
+      x1 *= r * (h < NG ? gq1 : gk1);
+      // angle pos * theta^(-2i/D) in double, reduced to [-pi, pi] in double,
+      // then cos/sin in single precision
+      const double ang = (double)pos * ifreq;
+      const double red2 = ang - 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
+      float sf, cf;
+      sincosf((float)red2, &sf, &cf);
       const float y0 = x0 * cf - x1 * sf, y1 = x1 * cf + x0 * sf;
       if (h < NG) {
         qs[h * D + lane] = y0 * G.attn_scale;
@@ -575,8 +662,7 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
 #pragma unroll
         for (int h = 0; h < 8; ++h) {
           if (h < NG) {
-            float s = part[h];
-            for (int o = 1; o < cpr; o <<= 1) s += __shfl_xor(s, o);
+            const float s = cpr == 16 ? row16_sum(part[h]) : row8_sum(part[h]);
             if (my_c == 0 && r < T) sc[h * SMAX + r] = s;
           }
         }
@@ -662,31 +748,76 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
     st_t(part + (size_t)tid * (D + 2), ml[2 * tid], a.tag);
     st_t(part + (size_t)tid * (D + 2) + 1, ml[2 * tid + 1], a.tag);
   }
+  if (op.aux) {
+    // fused merge: count this chunk's arrival; the last of the C chunks of
+    // (b, g) combines all partials (their words are tagged, so it can read
+    // them as soon as they land)
+    __syncthreads();
+    if (tid == 0) {
+      u32* arr = (u32*)op.aux + ((size_t)b * Hkv + g) * kCounterStride;
+      const u32 old = __hip_atomic_fetch_add(gp(arr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      c.flags[4] = old + 1u == (u32)C * (a.epoch + 1u) ? 1 : 0;
+    }
+    __syncthreads();
+    if (c.flags[4]) merge_partials(c, op.out, (u64*)op.aux2, b, g);
+  }
 }
 
 // ---------------------------------------------------------------- merge
 // attn[b][g*G+h][d] = sum_c e^{m_c - M} o_c[d] / sum_c e^{m_c - M} l_c
-DEV void body_merge(Ctx& c, const OpDesc& op) {
+// Three phases: (m, l) of every (chunk, head) into LDS; per head the max M and
+// the chunk weights e^{m_c - M} (computed once); then every output element
+// fetches its C partial values in one batch.
+//   attn[b][g*G+h][d] = sum_c e^{m_c - M} o_c[d] / sum_c e^{m_c - M} l_c
+DEV void merge_partials(Ctx& c, const u64* parts, u64* out, int b, int g) {
   const StepArgs& a = *c.a;
   const Geom& G = *a.geom;
-  const int b = c.t.a0, g = c.t.a1;
-  const int D = G.D, NG = G.G, C = G.C;
-  const u64* part = op.in + (((size_t)b * G.Hkv + g) * C) * NG * (size_t)(D + 2);
-  for (int j = threadIdx.x; j < NG * D; j += NT) {
-    const int h = j / D, dd = j - h * D;
+  const int D = G.D, NG = G.G, C = G.C, tid = threadIdx.x;
+  const u64* part = parts + (((size_t)b * G.Hkv + g) * C) * NG * (size_t)(D + 2);
+  float* wgt = (float*)c.lds + kStageFloats;  // [C][NG]: m, then e^{m - M}
+  float* lsum = wgt + C * NG;                 // [C][NG]: l
+  float* hsum = lsum + C * NG;                // [NG]: sum_c e^{m_c - M} l_c
+  for (int j = tid; j < C * NG; j += NT) {
+    const u64* p = part + (size_t)j * (D + 2);
+    const u64 wm = ld_raw(p), wl = ld_raw(p + 1);
+    wgt[j] = fix_t(wm, p, a);
+    lsum[j] = fix_t(wl, p + 1, a);
+  }
+  __syncthreads();
+  if (tid < NG) {
     float M = -INFINITY;
-    for (int ch = 0; ch < C; ++ch) M = fmaxf(M, ld_t(part + ((size_t)ch * NG + h) * (D + 2), a));
-    float L = 0.f, O = 0.f;
+    for (int ch = 0; ch < C; ++ch) M = fmaxf(M, wgt[ch * NG + tid]);
+    float L = 0.f;
     for (int ch = 0; ch < C; ++ch) {
-      const u64* p = part + ((size_t)ch * NG + h) * (D + 2);
-      const float m = ld_t(p, a);
-      if (m == -INFINITY) continue;
-      const float w = expf(m - M);
-      L = fmaf(w, ld_t(p + 1, a), L);
-      O = fmaf(w, ld_t(p + 2 + dd, a), O);
+      const float m = wgt[ch * NG + tid];
+      const float w = m == -INFINITY ? 0.f : expf(m - M);
+      wgt[ch * NG + tid] = w;
+      L = fmaf(w, lsum[ch * NG + tid], L);
     }
-    st_t(op.out + (size_t)b * G.Hq * D + ((size_t)g * NG + h) * D + dd, O / L, a.tag);
+    hsum[tid] = L;
+  }
+  __syncthreads();
+  constexpr int CH = 16;
+  for (int j = tid; j < NG * D; j += NT) {
+    const int h = j / D, dd = j - h * D;
+    const u64* p0 = part + (size_t)h * (D + 2) + 2 + dd;
+    const size_t cstride = (size_t)NG * (D + 2);
+    float O = 0.f;
+    for (int c0 = 0; c0 < C; c0 += CH) {
+      u64 w[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) w[i] = ld_raw(p0 + (size_t)min(c0 + i, C - 1) * cstride);
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if (c0 + i < C) {
+          const float wt = wgt[(c0 + i) * NG + h];
+          if (wt != 0.f) O = fmaf(wt, fix_t(w[i], p0 + (size_t)(c0 + i) * cstride, a), O);
+        }
+    }
+    st_t(out + (size_t)b * G.Hq * D + ((size_t)g * NG + h) * D + dd, O / hsum[h], a.tag);
   }
 }
+
+DEV void body_merge(Ctx& c, const OpDesc& op) { merge_partials(c, op.in, op.out, c.t.a0, c.t.a1); }
 
 }  // namespace mk

@@ -151,10 +151,18 @@ void build_decoder_ops(Graph& g) {
       }
     }
     // Attention chunks: (b, g, chunk); the last chunk appends the new k/v.
+    // Without merge tasks the op is joint: the last chunk of (b, g) to finish
+    // reads every chunk's partial and writes the merged heads.
+    const bool fused = g.opts.merge_tasks == 0;
     {
       int32_t o = bd.op(OP_ATTN, l, D, 0, 0);
       g.ops[o].in_buf = qkv;
       g.ops[o].out_buf = part;
+      if (fused) {
+        g.ops[o].joint = true;
+        g.ops[o].aux_buf = -3;  // arrival counters of this layer (separate scratch region)
+        g.ops[o].aux2_buf = attn;
+      }
       for (int32_t b = 0; b < B; ++b)
         for (int32_t gi = 0; gi < Hkv; ++gi)
           for (int32_t c = 0; c < C; ++c) {
@@ -162,9 +170,13 @@ void build_decoder_ops(Graph& g) {
             Builder::rd(t, qkv, (int64_t)b * QN + (int64_t)gi * RG, RG);
             Builder::wr(t, part, (((int64_t)b * Hkv + gi) * C + c) * PW, PW);
             if (c == C - 1) Builder::wr(t, kvnew, (int64_t)b * Hkv + gi, 1);
+            if (fused) {
+              Builder::rd(t, part, ((int64_t)b * Hkv + gi) * C * PW, (int64_t)C * PW);
+              Builder::wr(t, attn, (int64_t)b * Hq * D + (int64_t)gi * G * D, (int64_t)G * D);
+            }
           }
     }
-    {
+    if (!fused) {
       int32_t o = bd.op(OP_MERGE, l, D, 0, 0);
       g.ops[o].in_buf = part;
       g.ops[o].out_buf = attn;
@@ -869,6 +881,11 @@ void layout(Graph& g) {
   sc = align_up(sc + (int64_t)g.events.size() * kEventBytes, 256);
   g.off_status = sc;
   sc = align_up(sc + ST_WORDS * 4, 256);
+  g.off_progress = sc;  // one word per agent: 1 + id of the task it is in, 0xFFFFFFFF when done
+  sc = align_up(sc + (int64_t)(g.W + 1) * 4, 256);
+  g.off_arrive = sc;    // attention arrival counters: [L][B][Hkv] x one 128-byte line
+  sc = align_up(sc + (int64_t)g.shape.n_layers * g.B * g.shape.n_kv_heads * kCounterStride * 4, 256);
+  g.off_state_end = sc; // counters .. here are the event state cleared by a reset
   for (Buffer& b : g.bufs) {
     if (b.off == -2) continue;
     b.off = sc;
@@ -921,7 +938,7 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   if (batch <= 0 || batch > 16) return bad("batch must be in 1..16");
   if (cap <= 0 || cap > (1 << 20)) return bad("max_ctx out of range");
   if (workers <= 0 || workers > 4096) return bad("worker count out of range");
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 7; ++i)
     if (o.reserved[i]) return bad("reserved options must be zero");
 
   Graph* g = new Graph();
@@ -965,7 +982,8 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
     const int64_t G = s.n_q_heads / s.n_kv_heads;
     while ((int64_t)G * ((cap + C - 1) / C + 1) > kScoreFloats) ++C;
   }
-  g->C = std::min(C, 1024);
+  // the merge keeps 2 floats per (chunk, head) in a 32 KB LDS area
+  g->C = std::min(C, std::max(1, (kRowResultFloats - 16) / (2 * (s.n_q_heads / s.n_kv_heads))));
   build_decoder_ops(*g);
   if (!finish_graph(*g, err)) {
     delete g;

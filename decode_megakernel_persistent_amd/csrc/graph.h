@@ -76,7 +76,7 @@ struct Graph {
   std::vector<CopyJob> copies;
   int64_t arena_bytes = 0, scratch_bytes = 0, trace_bytes = 0;
   int64_t off_geom = 0, off_ops = 0, off_tasks = 0, off_events = 0, off_wloff = 0, off_wlids = 0, off_invfreq = 0;
-  int64_t off_counters = 0, off_status = 0;
+  int64_t off_counters = 0, off_status = 0, off_progress = 0, off_arrive = 0, off_state_end = 0;
   int64_t weight_bytes_step = 0;
 };
 

@@ -83,17 +83,25 @@ DEV bool entry_ok(const StepArgs& a, int* flags) {
   return flags[0] == 0;
 }
 
+// Register cap: two worker wavefronts per SIMD must leave room for the
+// dispatch wavefront (8 VGPRs) on whichever CU it runs, or the worker
+// workgroup of that CU could not become resident.
 template <int NB>
-__global__ void __launch_bounds__(NT, 1) mk_worker(StepArgs a) {
+__global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerVgprs))) mk_worker(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flags[64];
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.status + ST_ARRIVED, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (entry_ok(a, flags)) {
     const int w = blockIdx.x;
     for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
+      if (threadIdx.x == 0)
+        __hip_atomic_store(a.progress + w, (u32)a.wl_ids[k] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       run_task<NB>(a, a.wl_ids[k], w, false, lds, flags);
       __syncthreads();
       if (flags[0]) break;
     }
+    if (threadIdx.x == 0 && !flags[0])
+      __hip_atomic_store(a.progress + w, 0xFFFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (threadIdx.x == 0) __hip_atomic_fetch_add(a.status + ST_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -111,10 +119,30 @@ __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
 // watchdog budget.
 __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
   const int W = a.n_workers;
-  const int lane = threadIdx.x;
   const u32 target = (u32)W * (a.epoch + 1u);
-  const u64 t0 = wall_clock64();
-  (void)lane;
+  u64 t0 = wall_clock64();
+  // entry handshake: every worker workgroup must become resident while the
+  // others wait for it; give it a short budget, then report and abort
+  const u64 resident_budget = a.budget / 8 + 1;
+  for (;;) {
+    u32 arrived = __hip_atomic_load(a.status + ST_ARRIVED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived >= target) break;
+    if (__hip_atomic_load(a.status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+    if (wall_clock64() - t0 > resident_budget) {
+      if (threadIdx.x == 0) {
+        u32 z = 0;
+        if (__hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_NOT_RESIDENT, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          __hip_atomic_store(a.status + ST_SEEN, arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.status + ST_TARGET, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(a.status + ST_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
+    __builtin_amdgcn_s_sleep(16);
+  }
+  t0 = wall_clock64();
   for (;;) {
     u32 done = __hip_atomic_load(a.status + ST_DONE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done >= target) break;
@@ -369,6 +397,9 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
     d.out = bufp(o.out_buf);
     d.aux = bufp(o.aux_buf);
     d.aux2 = bufp(o.aux2_buf);
+    if (o.aux_buf == -3)  // attention arrival counters of layer o.layer
+      d.aux = (uint64_t*)(scratch + G.off_arrive +
+                          (int64_t)o.layer * G.B * G.shape.n_kv_heads * kCounterStride * 4);
   }
   HIPCHK(hipMemcpy(arena + G.off_ops, od.data(), od.size() * sizeof(OpDesc), hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(arena + G.off_tasks, G.tasks.data(), G.tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
@@ -380,6 +411,8 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   HIPCHK(hipMemsetAsync(scratch, 0, (size_t)G.scratch_bytes, stream));
   if (G.trace_bytes > 0) HIPCHK(hipMemsetAsync(d_trace, 0, (size_t)G.trace_bytes, stream));
   HIPCHK(hipStreamSynchronize(stream));
+  const u32 none = 0xFFFFFFFFu;
+  HIPCHK(hipMemcpy(scratch + G.off_status + ST_MIN_TASK * 4, &none, 4, hipMemcpyHostToDevice));
   int wcr = 0;
   HIPCHK(hipDeviceGetAttribute(&wcr, hipDeviceAttributeWallClockRate, dev));
   const int64_t us = G.opts.spin_timeout_us > 0 ? G.opts.spin_timeout_us : 2000000;
@@ -389,6 +422,18 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
     (void)hipFuncSetAttribute(lpt_fn(nb), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   }
   (void)hipGetLastError();
+  // co-residency: two worker wavefronts per SIMD plus the dispatch wavefront
+  {
+    hipFuncAttributes fw, fd;
+    HIPCHK(hipFuncGetAttributes(&fw, worker_fn(G.B)));
+    HIPCHK(hipFuncGetAttributes(&fd, (const void*)mk_dispatch));
+    auto gran = [](int v) { return (v + 7) / 8 * 8; };
+    if (2 * gran(fw.numRegs) + gran(fd.numRegs) > 512 || fw.localSizeBytes > 0) {
+      set_error("mk_load_weights: worker kernel uses " + std::to_string(fw.numRegs) + " VGPRs and " +
+                std::to_string(fw.localSizeBytes) + " B scratch; the dispatch wavefront would not fit beside it");
+      return MK_ERR_NOT_RESIDENT;
+    }
+  }
   g->arena = d_arena;
   g->scratch = d_scratch;
   g->trace = d_trace;
@@ -441,6 +486,7 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
   a.wl_ids = (const int32_t*)(arena + G.off_wlids);
   a.counters = (u32*)(scratch + G.off_counters);
   a.status = (u32*)(scratch + G.off_status);
+  a.progress = (u32*)(scratch + G.off_progress);
   a.tokens = d_tokens;
   a.positions = d_positions;
   a.kv_k = (uint16_t*)kv->k;
@@ -521,8 +567,47 @@ mk_status mk_check(mk_graph* g) {
       msg += ": the dispatcher saw " + std::to_string(st[ST_SEEN]) + " of " + std::to_string(st[ST_TARGET]) +
              " workers finish";
     } else {
-      msg += ": an activation word kept a stale tag";
+      const uint64_t addr = ((uint64_t)st[ST_ADDR_HI] << 32) | st[ST_ADDR_LO];
+      const uint64_t base = (uint64_t)(uintptr_t)g->scratch;
+      std::string where = "?";
+      for (const Buffer& b : G.bufs)
+        if (b.off >= 0 && addr >= base + b.off && addr < base + b.off + b.words * 8)
+          where = b.name + "[" + std::to_string((addr - base - b.off) / 8) + "]";
+      msg += ": activation word " + where + " kept tag " + std::to_string(st[ST_SEEN]) + " (want " +
+             std::to_string(st[ST_TARGET]) + ")";
     }
+    if (st[ST_ADDR_LO] | st[ST_ADDR_HI]) {
+      const uint64_t addr = ((uint64_t)st[ST_ADDR_HI] << 32) | st[ST_ADDR_LO];
+      const uint64_t base = (uint64_t)(uintptr_t)g->scratch;
+      for (const Buffer& b : G.bufs)
+        if (b.off >= 0 && addr >= base + b.off && addr < base + b.off + b.words * 8)
+          msg += "; stale word " + b.name + "[" + std::to_string((addr - base - b.off) / 8) + "]";
+    }
+    {
+      std::vector<u32> prog((size_t)G.W + 1);
+      if (hipMemcpy(prog.data(), (char*)g->scratch + G.off_progress, prog.size() * 4, hipMemcpyDeviceToHost) ==
+          hipSuccess) {
+        std::vector<std::pair<u32, int>> stuck;
+        for (int w = 0; w < G.W; ++w)
+          if (prog[w] != 0xFFFFFFFFu && prog[w] != 0) stuck.push_back({prog[w] - 1, w});
+        std::sort(stuck.begin(), stuck.end());
+        msg += "; " + std::to_string(stuck.size()) + " workers unfinished";
+        for (size_t i = 0; i < stuck.size() && i < 4; ++i) {
+          const u32 id = stuck[i].first;
+          msg += ", worker " + std::to_string(stuck[i].second) + " in task " + std::to_string(id);
+          if (id < G.tasks.size())
+            msg += std::string(" (") + op_kind_name(G.ops[G.tasks[id].op].kind) + ")";
+        }
+      }
+    }
+    const u32 mt = st[ST_MIN_TASK];
+    if (mt < (u32)G.tasks.size())
+      msg += "; most upstream timed-out task " + std::to_string(mt) + " (" + op_kind_name(G.ops[G.tasks[mt].op].kind) +
+             ", layer " + std::to_string(G.ops[G.tasks[mt].op].layer) + ")";
+  } else if (st[ST_ERROR] == ERR_NOT_RESIDENT) {
+    msg = "only " + std::to_string(st[ST_SEEN] % (u32)G.W) + " of " + std::to_string(G.W) +
+          " worker workgroups became resident (the dispatcher gave up waiting)";
+    rc = MK_ERR_NOT_RESIDENT;
   } else if (st[ST_ERROR] == ERR_CONFIG) {
     msg = "device tables do not match the graph (reload the weights)";
     rc = MK_ERR_STATE;
@@ -534,8 +619,10 @@ mk_status mk_check(mk_graph* g) {
     rc = MK_ERR_STATE;
   }
   // reset the event state so that the next step can run
-  HIPCHK(hipMemset((char*)g->scratch + G.off_counters, 0, (size_t)(G.off_status - G.off_counters) + ST_WORDS * 4));
+  HIPCHK(hipMemset((char*)g->scratch + G.off_counters, 0, (size_t)(G.off_state_end - G.off_counters)));
   HIPCHK(hipDeviceSynchronize());
+  const u32 none = 0xFFFFFFFFu;
+  HIPCHK(hipMemcpy((char*)g->scratch + G.off_status + ST_MIN_TASK * 4, &none, 4, hipMemcpyHostToDevice));
   g->epoch = 0;
   set_error("mk_check: " + msg);
   return rc;

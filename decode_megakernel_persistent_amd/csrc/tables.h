@@ -102,6 +102,10 @@ enum StatusWord : int32_t {
   ST_TICKET = 7,    // trace ticket (cumulative)
   ST_TRACE_N = 8,   // trace records of the current step
   ST_DISPATCH = 9,  // dispatcher progress (cumulative events seen)
+  ST_MIN_TASK = 10, // smallest task id whose wait timed out (0xFFFFFFFF = none)
+  ST_ADDR_LO = 11,  // address of a tagged word that never became current
+  ST_ADDR_HI = 12,
+  ST_ARRIVED = 13,  // worker workgroups that started (cumulative over steps)
   ST_WORDS = 64
 };
 
@@ -111,6 +115,9 @@ constexpr int kStageFloats = 24576;      // GEMV input staging (96 KB)
 constexpr int kRowResultFloats = 8192;   // GEMV per-row results (32 KB)
 constexpr int kScoreFloats = 8192;       // attention scores of one chunk (32 KB)
 
-enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT = 1, ERR_CONFIG = 2, ERR_BAD_TASK = 3, ERR_BAD_INPUT = 4 };
+enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT = 1, ERR_CONFIG = 2, ERR_BAD_TASK = 3, ERR_BAD_INPUT = 4, ERR_NOT_RESIDENT = 5 };
+
+// VGPR cap of the worker kernel: 2 x 248 + 8 (one dispatch wavefront) <= 512 per SIMD.
+constexpr int kWorkerVgprs = 248;
 
 }  // namespace mk

@@ -88,7 +88,9 @@ typedef struct {
   int32_t spin_timeout_us; /* watchdog budget of any single device wait; 0 = 2 s */
   int32_t no_fusion;       /* 1 = one event per dependency edge (analysis only: normalisation then
                               inserts empty tasks); 0 = fuse events (default) */
-  int32_t reserved[8];     /* must be zero */
+  int32_t merge_tasks;     /* 1 = separate attention-merge tasks; 0 = the last chunk of each
+                              (sequence, kv head) to finish merges the partials (default) */
+  int32_t reserved[7];     /* must be zero */
 } mk_build_opts;
 
 /* One logical tensor handed to mk_load_weights.  Names:

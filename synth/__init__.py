@@ -41,7 +41,7 @@ def build(verbose: bool = False) -> str:
     import subprocess
 
     src = os.path.join(_HERE, "synth.c")
-    cmd = ["gcc", "-O2", "-shared", "-fPIC", "-pthread", "-o", _LIB_PATH, src, "-lm"]
+    cmd = ["gcc", "-O3", "-shared", "-fPIC", "-pthread", "-o", _LIB_PATH, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

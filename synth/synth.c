@@ -15,10 +15,13 @@
  *   draw(seed,key,i)  = mix64(mix64(mix64(seed) ^ key) ^ i)
  *   key(name)         = 64-bit FNV-1a of the tensor name's bytes
  *   unit53(u)         = (u >> 11) * 2^-53                    in [0, 1)
- *   normal pair j     : u1 = 1 - unit53(draw(..,2j)) in (0,1], u2 = unit53(draw(..,2j+1))
- *                       r = sqrt(-2 ln u1); element 2j = r cos(2 pi u2),
- *                       element 2j+1 = r sin(2 pi u2)        (Box-Muller, double)
- *   bf16 value        = round-to-nearest-even of the float nearest to sigma*z
+ *   unit24(u)         = (u >> 40) * 2^-24                    in [0, 1)
+ *   normal pair j     : u1 = 1 - unit24(draw(..,2j)) in (0,1], u2 = unit24(draw(..,2j+1))
+ *                       r = sqrtf(-2 logf(u1)); a = 2 pi u2 (float);
+ *                       element 2j = r cosf(a), element 2j+1 = r sinf(a)
+ *                       (Box-Muller in single precision: every value is
+ *                       rounded to bf16 afterwards)
+ *   bf16 value        = round-to-nearest-even of the float sigma*z
  *   uniform int       = lo + floor(unit53(draw(seed,key,i)) * (hi - lo + 1))
  */
 #include <math.h>
@@ -36,7 +39,9 @@ static inline uint64_t mix64(uint64_t z) {
   return z;
 }
 
-uint64_t synth_draw(uint64_t seed, uint64_t key, uint64_t i) { return mix64(mix64(mix64(seed) ^ key) ^ i); }
+static inline uint64_t draw(uint64_t seed, uint64_t key, uint64_t i) { return mix64(mix64(mix64(seed) ^ key) ^ i); }
+
+uint64_t synth_draw(uint64_t seed, uint64_t key, uint64_t i) { return draw(seed, key, i); }
 
 uint64_t synth_key(const char* name) {
   uint64_t h = 0xcbf29ce484222325ull;
@@ -58,13 +63,21 @@ static inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(x >> 16);
 }
 
+static inline float unit24(uint64_t u) { return (float)(u >> 40) * (1.0f / 16777216.0f); }
+
+static inline void normal_pair(uint64_t seed, uint64_t key, uint64_t pair, float* z0, float* z1) {
+  float u1 = 1.0f - unit24(draw(seed, key, 2 * pair));
+  float u2 = unit24(draw(seed, key, 2 * pair + 1));
+  float r = sqrtf(-2.0f * logf(u1));
+  float a = 6.28318530717958647692f * u2;
+  *z0 = r * cosf(a);
+  *z1 = r * sinf(a);
+}
+
 double synth_normal(uint64_t seed, uint64_t key, uint64_t idx) {
-  uint64_t j = idx >> 1;
-  double u1 = 1.0 - unit53(synth_draw(seed, key, 2 * j));
-  double u2 = unit53(synth_draw(seed, key, 2 * j + 1));
-  double r = sqrt(-2.0 * log(u1));
-  double a = 6.283185307179586476925286766559 * u2;
-  return (idx & 1) ? r * sin(a) : r * cos(a);
+  float z0, z1;
+  normal_pair(seed, key, idx >> 1, &z0, &z1);
+  return (idx & 1) ? z1 : z0;
 }
 
 typedef struct {
@@ -72,7 +85,7 @@ typedef struct {
   int64_t begin, end; /* element range of this worker, relative to out */
   int64_t start;      /* global element index of out[0] */
   uint64_t seed, key;
-  double sigma;
+  float sigma;
 } normal_job;
 
 static void* normal_worker(void* arg) {
@@ -81,18 +94,14 @@ static void* normal_worker(void* arg) {
   /* elements come in Box-Muller pairs; compute both halves of a pair at once */
   while (i < j->end) {
     uint64_t g = (uint64_t)(j->start + i);
-    uint64_t pair = g >> 1;
-    double u1 = 1.0 - unit53(synth_draw(j->seed, j->key, 2 * pair));
-    double u2 = unit53(synth_draw(j->seed, j->key, 2 * pair + 1));
-    double r = sqrt(-2.0 * log(u1));
-    double a = 6.283185307179586476925286766559 * u2;
+    float z0, z1;
+    normal_pair(j->seed, j->key, g >> 1, &z0, &z1);
     if ((g & 1) == 0 && i + 1 < j->end) {
-      j->out[i] = f32_to_bf16_rne((float)(j->sigma * (r * cos(a))));
-      j->out[i + 1] = f32_to_bf16_rne((float)(j->sigma * (r * sin(a))));
+      j->out[i] = f32_to_bf16_rne(j->sigma * z0);
+      j->out[i + 1] = f32_to_bf16_rne(j->sigma * z1);
       i += 2;
     } else {
-      double z = (g & 1) ? r * sin(a) : r * cos(a);
-      j->out[i] = f32_to_bf16_rne((float)(j->sigma * z));
+      j->out[i] = f32_to_bf16_rne(j->sigma * ((g & 1) ? z1 : z0));
       i += 1;
     }
   }
@@ -115,7 +124,7 @@ int synth_fill_normal_bf16(uint16_t* out, int64_t n, uint64_t seed, uint64_t key
     int64_t b = (int64_t)t * per, e = b + per;
     if (b >= n) break;
     if (e > n) e = n;
-    jobs[t] = (normal_job){out, b, e, start, seed, key, sigma};
+    jobs[t] = (normal_job){out, b, e, start, seed, key, (float)sigma};
     if (nthreads == 1) {
       normal_worker(&jobs[t]);
     } else {
@@ -133,7 +142,7 @@ int synth_fill_uniform_i32(int32_t* out, int64_t n, uint64_t seed, uint64_t key,
   if (hi < lo) return -1;
   double span = (double)hi - (double)lo + 1.0;
   for (int64_t i = 0; i < n; ++i) {
-    int64_t v = (int64_t)lo + (int64_t)floor(unit53(synth_draw(seed, key, (uint64_t)(start + i))) * span);
+    int64_t v = (int64_t)lo + (int64_t)floor(unit53(draw(seed, key, (uint64_t)(start + i))) * span);
     if (v > hi) v = hi;
     out[i] = (int32_t)v;
   }

@@ -18,8 +18,9 @@ from tests import harness
 pytestmark = pytest.mark.gpu
 
 
-def run_steps(w, prep, mode, steps, trace=True, workers=0, gemv=mk.MK_GEMV_AUTO, attn_chunks=0):
-    opts = mk.make_opts(mode=mode, trace=int(trace), num_workers=workers, gemv=gemv, attn_chunks=attn_chunks)
+def run_steps(w, prep, mode, steps, trace=True, workers=0, gemv=mk.MK_GEMV_AUTO, attn_chunks=0, merge_tasks=0):
+    opts = mk.make_opts(mode=mode, trace=int(trace), num_workers=workers, gemv=gemv, attn_chunks=attn_chunks,
+                        merge_tasks=merge_tasks)
     sess = mk.Session(w.shape, w.batch, w.capacity, opts)
     try:
         sess.load(prep.weights)
@@ -78,9 +79,34 @@ def test_tiny_small_worker_count(tiny):
     assert_reports(reports)
 
 
+def test_tiny_separate_merge_tasks(tiny):
+    w, prep = tiny
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=3, merge_tasks=1)
+    assert_reports(reports)
+
+
 def test_tiny_one_chunk_and_many_chunks(tiny):
     w, prep = tiny
     for C in (1, 7):
         reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=2, attn_chunks=C)
         assert st.attn_chunks == C
         assert_reports(reports)
+
+
+@pytest.fixture(scope="module", params=["qwen3-0.6b", "qwen3-1.7b", "qwen3-8b"])
+def dense(request):
+    w = synth.WORKLOADS[request.param]
+    return w, harness.prepare(w)
+
+
+def test_dense_parity_persistent(dense):
+    w, prep = dense
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=4)
+    assert st.empty_tasks == 0
+    assert_reports(reports)
+
+
+def test_dense_parity_launch_per_task(dense):
+    w, prep = dense
+    reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=2, trace=False)
+    assert_reports(reports)

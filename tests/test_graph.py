@@ -1,0 +1,211 @@
+"""The host task-graph compiler and the event protocol, on the CPU.
+
+Invariants of the compiled tables (MPK review page 2512.22219, section 2.4):
+every task has at most one dependency event and one trigger event, each
+event's dependents are one contiguous id range, ids are topological, each
+event's target equals its number of triggering tasks.  Edge preservation is
+checked by brute force: every read/write conflict edge derived from the
+tasks' footprints is implied by a path in the final event graph.  The
+protocol itself runs on host threads (the same tables, no-op bodies) and the
+trace checker must accept clean runs and flag planted faults.
+"""
+
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import decode_megakernel_persistent_amd as mk
+import synth
+
+TINY = synth.WORKLOADS["tiny"]
+SMALL = synth.ModelShape(n_layers=3, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
+                         vocab=2048, tied_embeddings=True)
+MOE = synth.ModelShape(n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=64, intermediate=0, vocab=1024,
+                       tied_embeddings=False, n_experts=16, top_k=4, expert_intermediate=128)
+
+
+def build(shape, batch=1, cap=64, **kw):
+    kw.setdefault("num_workers", 16)
+    return mk.mk_build_graph(shape, batch, cap, mk.make_opts(**kw))
+
+
+def check_invariants(g):
+    tasks = mk.mk_get_tasks(g)
+    ev = mk.mk_get_events(g)
+    off, ids = mk.mk_get_worker_lists(g)
+    n, ne = len(tasks), len(ev)
+    dep, trig = tasks[:, 2], tasks[:, 3]
+    assert dep.min() >= -1 and dep.max() < ne and trig.min() >= -1 and trig.max() < ne
+    counts = np.bincount(trig[trig >= 0], minlength=ne)
+    np.testing.assert_array_equal(ev[:, 0], counts)            # need == number of triggers
+    for e, (need, first, last, prod) in enumerate(ev):
+        assert need >= 1
+        members = np.nonzero(dep == e)[0]
+        if last >= first:
+            np.testing.assert_array_equal(members, np.arange(first, last + 1))  # contiguous range
+            assert np.nonzero(trig == e)[0].max() < first                      # topological
+        else:
+            assert members.size == 0
+    # worker lists: a partition of the ids, each increasing
+    assert sorted(ids.tolist()) == list(range(n))
+    for w in range(len(off) - 1):
+        lst = ids[off[w]:off[w + 1]]
+        assert np.all(np.diff(lst) > 0)
+    return tasks, ev
+
+
+def ancestors_matrix(tasks, ev):
+    n = len(tasks)
+    anc = np.zeros((n, n), dtype=bool)
+    prods = [[] for _ in range(len(ev))]
+    for t in range(n):
+        if tasks[t, 3] >= 0:
+            prods[tasks[t, 3]].append(t)
+    for t in range(n):  # ids are topological
+        e = tasks[t, 2]
+        for p in prods[e] if e >= 0 else []:
+            anc[t, p] = True
+            anc[t] |= anc[p]
+    return anc
+
+
+@pytest.mark.parametrize("shape,batch,kw", [
+    (TINY.shape, 1, {}),
+    (TINY.shape, 1, {"merge_tasks": 1}),
+    (TINY.shape, 3, {"attn_chunks": 3}),
+    (SMALL, 2, {"num_workers": 7}),
+    (MOE, 2, {"num_workers": 8}),
+])
+def test_invariants_and_edge_preservation(shape, batch, kw):
+    g = build(shape, batch, **kw)
+    try:
+        tasks, ev = check_invariants(g)
+        raw = mk.mk_get_raw_edges(g)
+        assert len(raw) > 0
+        anc = ancestors_matrix(tasks, ev)
+        implied = anc[raw[:, 1], raw[:, 0]]
+        assert implied.all(), f"{(~implied).sum()} footprint edges not implied by the event graph"
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+def test_decoder_graphs_need_no_empty_tasks_and_fusion_shrinks_events():
+    g = build(TINY.shape)
+    try:
+        st = mk.mk_graph_stats(g)
+        assert st.empty_tasks == 0                      # deep, not wide
+        assert st.events < 10 * TINY.shape.n_layers
+    finally:
+        mk.mk_destroy_graph(g)
+    g = build(TINY.shape, no_fusion=1, num_workers=4)
+    try:
+        st2 = mk.mk_graph_stats(g)
+        assert st2.empty_tasks > 0 and st2.events > 10 * st.events
+        tasks, ev = check_invariants(g)                 # normalisation restores <=1 dep / <=1 trigger
+        raw = mk.mk_get_raw_edges(g)
+        anc = ancestors_matrix(tasks, ev)
+        assert anc[raw[:, 1], raw[:, 0]].all()
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+def test_head_group_aligned_qkv_tiles():
+    # each attention task depends on exactly the QKV tiles of its own kv head
+    g = build(SMALL, 1, num_workers=16)
+    try:
+        tasks, ev = check_invariants(g)
+        kinds = [mk.OP_KINDS[k] for k in tasks[:, 0]]
+        G = SMALL.n_q_heads // SMALL.n_kv_heads
+        rows_per_group = (G + 2) * SMALL.head_dim
+        for t in np.nonzero(np.array(kinds) == "attn")[0][:8]:
+            e = tasks[t, 2]
+            prods = np.nonzero(tasks[:, 3] == e)[0]
+            groups = {tasks[p, 5] // rows_per_group for p in prods}
+            assert groups == {tasks[t, 5]}
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+@pytest.mark.parametrize("merge_tasks", [0, 1])
+def test_8b_graph_shape_counts(merge_tasks):
+    s = synth.WORKLOADS["qwen3-8b"]
+    g = mk.mk_build_graph(s.shape, 1, s.capacity, mk.make_opts(num_workers=256, merge_tasks=merge_tasks))
+    try:
+        st = mk.mk_graph_stats(g)
+        # per layer: 256 QKV + 256 attention chunks (+ 8 merges) + 256 O + 256 gate-up + 256 down
+        assert st.tasks == 1 + 36 * (256 * 5 + 8 * merge_tasks) + 256
+        assert st.empty_tasks == 0
+        # per layer: QKV, 8 head groups, (8 merges), O, gate-up, down
+        assert st.events == 36 * (12 + 8 * merge_tasks) + 1
+        assert st.launches_per_step == st.events + 1
+        assert st.max_tasks_per_worker <= 36 * 6 + 2
+        assert abs(st.weight_bytes / 1e9 - 15.137) < 0.01
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+@pytest.mark.parametrize("shape,batch", [(TINY.shape, 1), (MOE, 2)])
+def test_simulated_protocol_traces_pass(shape, batch):
+    g = build(shape, batch, num_workers=8)
+    try:
+        recs, cnt = mk.mk_simulate(g, steps=3)
+        mk.mk_check_trace(g, recs, 2, cnt)
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+@pytest.mark.parametrize("fault,status", [(1, mk.MK_ERR_TIMEOUT), (2, mk.MK_ERR_TRACE), (3, mk.MK_ERR_TRACE)])
+def test_checker_catches_planted_faults(fault, status):
+    g = build(TINY.shape, num_workers=8)
+    try:
+        with pytest.raises(mk.MkError) as e:
+            recs, cnt = mk.mk_simulate(g, steps=1, fault=fault, timeout_ms=300)
+            mk.mk_check_trace(g, recs, 0, cnt)
+        assert e.value.status == status
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+def test_checker_rejects_tampered_traces():
+    g = build(TINY.shape, num_workers=8)
+    try:
+        recs, cnt = mk.mk_simulate(g, steps=1)
+        mk.mk_check_trace(g, recs, 0, cnt)
+        dup = recs.copy()
+        dup[1] = dup[0]
+        with pytest.raises(mk.MkError, match="more than once"):
+            mk.mk_check_trace(g, dup, 0, cnt)
+        with pytest.raises(mk.MkError, match="records"):
+            mk.mk_check_trace(g, recs[:-1], 0, cnt)
+        low = recs.copy()
+        k = int(np.nonzero(mk.mk_get_tasks(g)[low["task"], 2] >= 0)[0][0])
+        low["dep_seen"][k] = 0
+        with pytest.raises(mk.MkError, match="below target"):
+            mk.mk_check_trace(g, low, 0, cnt)
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+def test_protocol_under_thread_sanitizer(tmp_path):
+    from decode_megakernel_persistent_amd import build as b
+    exe = b.build_tsan()
+    r = subprocess.run([exe, "8", "3"], capture_output=True, text=True, timeout=600,
+                       env={**os.environ, "TSAN_OPTIONS": "halt_on_error=1"})
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "WARNING: ThreadSanitizer" not in r.stderr
+    assert r.stdout.count("ok") == 2
+
+
+def test_dump_graph_json(tmp_path):
+    import json
+    g = build(TINY.shape)
+    try:
+        p = str(tmp_path / "g.json")
+        mk.mk_dump_graph(g, p)
+        d = json.load(open(p))
+        assert len(d["tasks"]) == mk.mk_graph_stats(g).tasks
+        assert d["gemv"] == "valu"
+    finally:
+        mk.mk_destroy_graph(g)

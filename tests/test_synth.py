@@ -41,18 +41,25 @@ def test_key_and_draw_definition():
 
 
 def test_normal_definition_box_muller():
+    # the stated single-precision Box-Muller, re-implemented with numpy float32;
+    # libm and numpy may differ by an ulp in logf/cosf, which can move a value
+    # across a bf16 rounding boundary, so a few one-ulp differences are allowed
     name, seed, sigma = "layers.0.wk", 0, 0.02
-    got = synth.normal_bf16(name, 64, seed, sigma, start=10, threads=1)
+    n, start = 4096, 10
+    got = synth.normal_bf16(name, n, seed, sigma, start=start, threads=1)
     key = fnv1a(name)
-    want = []
-    for idx in range(10, 74):
-        j = idx >> 1
-        u1 = 1.0 - (draw(seed, key, 2 * j) >> 11) * 2.0 ** -53
-        u2 = (draw(seed, key, 2 * j + 1) >> 11) * 2.0 ** -53
-        r = math.sqrt(-2.0 * math.log(u1))
-        z = r * (math.sin(2 * math.pi * u2) if idx & 1 else math.cos(2 * math.pi * u2))
-        want.append(sigma * z)
-    np.testing.assert_array_equal(got, synth.f32_to_bf16(np.array(want, dtype=np.float32)))
+    idx = np.arange(start, start + n)
+    pairs = idx >> 1
+    d1 = np.array([draw(seed, key, int(2 * j)) for j in pairs], dtype=np.uint64)
+    d2 = np.array([draw(seed, key, int(2 * j + 1)) for j in pairs], dtype=np.uint64)
+    u1 = np.float32(1.0) - (d1 >> np.uint64(40)).astype(np.float32) * np.float32(2.0 ** -24)
+    u2 = (d2 >> np.uint64(40)).astype(np.float32) * np.float32(2.0 ** -24)
+    r = np.sqrt(np.float32(-2.0) * np.log(u1))
+    a = np.float32(6.28318530717958647692) * u2
+    z = np.where(idx & 1, r * np.sin(a), r * np.cos(a)).astype(np.float32)
+    want = synth.f32_to_bf16(np.float32(sigma) * z)
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1 and np.count_nonzero(diff) <= n // 100
 
 
 def test_deterministic_across_threads_and_slices():
