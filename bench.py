@@ -6,7 +6,7 @@
 One step is one full decode step of the workload (embedding, every layer's
 RMSNorm/QKV/QK-norm+RoPE+KV-append/attention/merge/O/SwiGLU MLP, final norm
 and lm_head) on synthetic inputs already resident in HBM.  Prints one JSON
-line: ms/token (median over the timed steps, per-step HIP events on the
+line: ms/token (mean over the timed steps, per-step HIP events on the
 launching stream) and the algorithmic HBM bandwidth of the step (weights read
 + KV read + KV written + logits, divided by the step time) against MI355X's
 8 TB/s peak, the same step in launch-per-task mode, and the oracle's ms/token
@@ -16,7 +16,6 @@ on the host cores over a bounded sample.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -29,15 +28,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_qwen3-8b_b1.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mk_worker_qwen3-8b_b1_traffic.txt")
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("device.h", "runtime.hip", "graph.cpp", "tables.h"):
-        with open(os.path.join(ROOT, "decode_megakernel_persistent_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(shape, batch: int, positions: np.ndarray, weight_bytes: int) -> float:
@@ -54,10 +47,13 @@ def algorithmic_bytes(shape, batch: int, positions: np.ndarray, weight_bytes: in
 
 
 def time_steps(sess, tok_dev, pos0: np.ndarray, warmup: int, steps: int):
+    """Per-step HIP events on the stream the step is launched on (the
+    session's stream is torch's current stream), bracketing exactly the
+    decode_step enqueue; the next step's token/position copies sit outside."""
     import torch
     st = torch.cuda.current_stream()
     pos = torch.as_tensor(pos0.astype(np.int32), device=sess.device)
-    times, pos_list = [], []
+    pos_list = []
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(warmup):
@@ -80,6 +76,20 @@ def time_steps(sess, tok_dev, pos0: np.ndarray, warmup: int, steps: int):
     sess.check()
     times = [a.elapsed_time(b) for a, b in ev]
     return times, pos_list, wall
+
+
+def calibrate_copy(mib: int, reps: int = 3) -> None:
+    """Plain device-to-device copies of a known size (each reads and writes
+    `mib` MiB once) for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration copies: {reps} x {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(w, weights, kv_k, kv_v, tokens0, pos0, budget_s: float):
@@ -112,6 +122,10 @@ def main():
     ap.add_argument("--no-lpt", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-only", action="store_true", help="persistent steps only (for profilers)")
+    ap.add_argument("--no-watchdog", action="store_true",
+                    help="launch no dispatch wavefront (for counter runs, which serialise dispatches)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the steps, run plain copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); use --gpus 1",
@@ -143,7 +157,7 @@ def main():
     toks = synth.tokens(w, ntok)  # [B, ntok]
     print(f"[bench] inputs ready in {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
 
-    sess = mk.Session(s, B, cap, mk.make_opts(mode=mk.MK_PERSISTENT))
+    sess = mk.Session(s, B, cap, mk.make_opts(mode=mk.MK_PERSISTENT, no_watchdog=int(args.no_watchdog)))
     sess.load(weights)
     sess.set_kv(kv_k, kv_v)
     tok_dev = torch.as_tensor(toks.T.copy(), device=sess.device)  # [ntok, B]
@@ -156,11 +170,15 @@ def main():
     mean = statistics.fmean(times)
     bytes_steps = [algorithmic_bytes(s, B, p, sess.stats.weight_bytes) for p in pos_list]
     bytes_mean = statistics.fmean(bytes_steps)
-    gbs = [b / (t * 1e-3) / 1e9 for b, t in zip(bytes_steps, times)]
-    achieved = statistics.median(gbs)
-    print(f"[bench] persistent: median {med:.3f} ms/step, mean {mean:.3f}, {achieved:.0f} GB/s", file=sys.stderr,
-          flush=True)
+    # algorithmic bytes per launch / the average launch duration
+    achieved = bytes_mean / (mean * 1e-3) / 1e9
+    print(f"[bench] persistent: mean {mean:.4f} ms/step, median {med:.4f}, {achieved:.0f} GB/s "
+          f"({bytes_mean / 1e9:.3f} GB/step), wall {wall:.3f}s for {args.steps} steps", file=sys.stderr, flush=True)
     if args.profile_only:
+        sess.close()
+        if args.calibrate_copy:
+            calibrate_copy(args.calibrate_copy)
+        print("[bench] profile run done", file=sys.stderr, flush=True)
         return
 
     lpt = None
@@ -168,20 +186,21 @@ def main():
         sess.set_kv(kv_k, kv_v)
         sess.set_mode(mk.MK_LAUNCH_PER_TASK)
         t_l, _, _ = time_steps(sess, tok_dev, pos0, args.warmup, args.steps)
-        med_l = statistics.median(t_l)
-        lpt = {"ms_per_step": round(med_l, 4), "mean_ms": round(statistics.fmean(t_l), 4),
+        mean_l = statistics.fmean(t_l)
+        lpt = {"ms_per_step": round(mean_l, 4), "median_ms": round(statistics.median(t_l), 4),
                "launches_per_step": int(sess.stats.launches_per_step),
-               "persistent_speedup": round(med_l / med, 3),
-               "overhead_share": round(1.0 - med / med_l, 4)}
-        print(f"[bench] launch-per-task: median {med_l:.3f} ms/step", file=sys.stderr, flush=True)
+               "persistent_speedup": round(mean_l / mean, 3),
+               "overhead_share": round(1.0 - mean / mean_l, 4)}
+        print(f"[bench] launch-per-task: mean {mean_l:.4f} ms/step", file=sys.stderr, flush=True)
         sess.set_mode(mk.MK_PERSISTENT)
 
     traffic = None
-    if os.path.exists(PROFILE_TRAFFIC) and args.workload == "qwen3-8b":
-        with open(PROFILE_TRAFFIC) as fh:
-            prof = json.load(fh)
-        if prof.get("source_hash") == source_hash():
-            traffic = prof.get("bytes_per_launch")
+    if os.path.exists(PROFILE_TRAFFIC) and args.workload == "qwen3-8b" and B == 1:
+        from decode_megakernel_persistent_amd import profsum
+        prof = profsum.read_kv(PROFILE_TRAFFIC)
+        # counters taken on the kernels as they are now, else null
+        if prof.get("source_hash") == mk.source_hash():
+            traffic = int(float(prof["traffic_bytes_per_launch"]))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -196,13 +215,13 @@ def main():
 
     out = {
         "metric": "decode ms/token and weight-stream HBM GB/s vs peak, batch 1 (1 GPU)",
-        "value": round(med / B, 4),
+        "value": round(mean / B, 4),
         "unit": "ms/token",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(med, 4),
-        "mean_ms_per_step": round(mean, 4),
+        "ms_per_step": round(mean, 4),
+        "median_ms_per_step": round(med, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -215,10 +234,11 @@ def main():
         "hbm_frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": round(bytes_mean), "kernel": "mk_worker"},
+                     "algorithmic_bytes_per_launch": round(bytes_mean), "kernel": "mk_worker",
+                     "launch_ms": round(mean, 4)},
         "launch_per_task": lpt,
         "cpu_baseline": cpu,
-        "tokens_per_s": round(B * 1000.0 / med, 2),
+        "tokens_per_s": round(B * 1000.0 / mean, 2),
     }
     print(json.dumps(out))
 

@@ -21,6 +21,17 @@ import torch  # noqa: F401  (loads the HIP runtime libmk.so must share)
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmk.so")
 
+
+def source_hash() -> str:
+    """Hash of the sources the device kernels and their tables are built from
+    (ties profiler counters to the kernels they were taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("device.h", "runtime.hip", "graph.cpp", "graph.h", "tables.h"):
+        with open(os.path.join(_PKG, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 MK_OK = 0
 MK_ERR_ARG = -1
 MK_ERR_SHAPE = -2
@@ -55,7 +66,7 @@ class mk_build_opts(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("per_task_launch", ctypes.c_int32), ("num_workers", ctypes.c_int32),
                 ("trace", ctypes.c_int32), ("attn_chunks", ctypes.c_int32), ("gemv", ctypes.c_int32),
                 ("spin_timeout_us", ctypes.c_int32), ("no_fusion", ctypes.c_int32), ("merge_tasks", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 7)]
+                ("no_watchdog", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
 
 
 class mk_tensor(ctypes.Structure):
@@ -155,11 +166,11 @@ def make_shape(s) -> mk_model_shape:
 
 
 def make_opts(mode=MK_PERSISTENT, per_task_launch=0, num_workers=0, trace=0, attn_chunks=0, gemv=MK_GEMV_AUTO,
-              spin_timeout_us=0, no_fusion=0, merge_tasks=0) -> mk_build_opts:
+              spin_timeout_us=0, no_fusion=0, merge_tasks=0, no_watchdog=0) -> mk_build_opts:
     o = mk_build_opts()
     o.mode, o.per_task_launch, o.num_workers, o.trace = mode, per_task_launch, num_workers, trace
     o.attn_chunks, o.gemv, o.spin_timeout_us, o.no_fusion = attn_chunks, gemv, spin_timeout_us, no_fusion
-    o.merge_tasks = merge_tasks
+    o.merge_tasks, o.no_watchdog = merge_tasks, no_watchdog
     return o
 
 

@@ -90,7 +90,11 @@ typedef struct {
                               inserts empty tasks); 0 = fuse events (default) */
   int32_t merge_tasks;     /* 1 = separate attention-merge tasks; 0 = the last chunk of each
                               (sequence, kv head) to finish merges the partials (default) */
-  int32_t reserved[7];     /* must be zero */
+  int32_t no_watchdog;     /* 1 = persistent mode launches no dispatch wavefront (no residency
+                              handshake, no step watchdog; the workers' own bounded waits remain).
+                              For profilers that serialise kernel dispatches.  Rejected with
+                              MK_ERR_ARG when the graph has dispatcher tasks (routed experts). */
+  int32_t reserved[6];     /* must be zero */
 } mk_build_opts;
 
 /* One logical tensor handed to mk_load_weights.  Names:
