@@ -58,6 +58,15 @@ struct StepArgs {
   int32_t n_workers;
 };
 
+// Thread index behind an empty asm: index math derived from it stays inside
+// the task body instead of being hoisted out of the worker's task loop, where
+// it would hold registers through every other body.
+DEV int task_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // ---------------------------------------------------------------- scalars
 DEV float bf_lo(u32 v) { return __uint_as_float(v << 16); }
 DEV float bf_hi(u32 v) { return __uint_as_float(v & 0xffff0000u); }
@@ -174,6 +183,7 @@ struct Ctx {
   bool lpt;
   char* lds;     // dynamic LDS (kLdsBytes)
   int* flags;    // small static LDS block: [0] abort, [1] seen, [2] start ticket, [3] start clock
+  const int* pos;  // this step's positions, copied to LDS at kernel entry
 };
 
 DEV u32 event_total(const StepArgs& a, int ev, int lane) {
@@ -318,7 +328,7 @@ DEV void body_embed(Ctx& c, const OpDesc& op) {
 template <int NB>
 DEV void stage_input(Ctx& c, const OpDesc& op, float* xs, float* red) {
   const StepArgs& a = *c.a;
-  const int K = op.K, tid = threadIdx.x;
+  const int K = op.K, tid = task_tid();
   constexpr int CH = 8;  // tagged words in flight per thread
   const bool nrm = op.norm_in != 0;
   float ss[NB];
@@ -369,7 +379,7 @@ DEV void stage_input(Ctx& c, const OpDesc& op, float* xs, float* red) {
 // Residual words of this thread's first epilogue output, loaded right after
 // the wait so that the load overlaps the weight stream.
 DEV u64 gemv_residual_prefetch(const Ctx& c, const OpDesc& op, int NB) {
-  const int nr = c.t.a2, j = threadIdx.x;
+  const int nr = c.t.a2, j = task_tid();
   if ((op.kind != OP_OPROJ && op.kind != OP_DOWN) || j >= NB * nr) return 0ull;
   const int b = j / nr, row = c.t.a1 + (j - b * nr);
   return ld_raw(op.res + (size_t)b * op.N + row);
@@ -422,7 +432,7 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   const int K = op.K, CPR = K >> 3, NCH = (CPR + 63) >> 6, SPR = NCH / S;
   const bool gu = op.kind == OP_GATEUP;
   const int NR = gu ? 2 * t.a2 : t.a2;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
   const int nrw = NR > wave ? (NR - wave + NWAVE - 1) / NWAVE : 0;
   const int NSEG = nrw * SPR;
   const uint16_t* Wt = op.w + (size_t)(u32)t.a3;
@@ -512,21 +522,100 @@ DEV void gemv_valu_any(Ctx& c, const OpDesc& op) {
   else gemv_valu<NB, 1>(c, op);
 }
 
-DEV void merge_partials(Ctx& c, const u64* parts, u64* out, int b, int g);
+// ---------------------------------------------------------------- group reductions
+// Reduction over aligned groups of Lc lanes (Lc a power of two <= 64, uniform
+// across the wavefront; every lane of the group receives the result).  Steps
+// inside a 16-lane row use DPP; the 32- and 64-lane steps use the CDNA4
+// permlane swaps, which exchange rows between two registers.
+template <bool MAX>
+DEV float grp_op(float x, float y) { return MAX ? fmaxf(x, y) : x + y; }
+template <bool MAX>
+DEV float group_reduce(float v, int Lc) {
+  if (Lc >= 2) v = grp_op<MAX>(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  if (Lc >= 4) v = grp_op<MAX>(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  if (Lc >= 8) v = grp_op<MAX>(v, dpp<0x141>(v));  // row_half_mirror
+  if (Lc >= 16) v = grp_op<MAX>(v, dpp<0x140>(v)); // row_mirror
+  if (Lc >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = grp_op<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if (Lc >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = grp_op<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
+}
 
-// ---------------------------------------------------------------- attention
-// One (sequence b, kv head g, chunk) task: q-norm + RoPE for the G query
-// heads; in the last chunk also k-norm + RoPE of the new key, bf16 rounding,
-// and the KV-cache append at position p; then scores, a chunk-local softmax
-// (max m, sum l) and the unnormalised output o for each head.
-// Rows of the chunk are read 16 bytes per lane: D/8 lanes per row.
-DEV void body_attn(Ctx& c, const OpDesc& op) {
+// ---------------------------------------------------------------- merge
+// Combine the C chunk partials of (sequence b, kv head group gi) for outputs
+// k in [k0, k0 + n) of the group (k = h * D + d).  Each chunk left, per head,
+// its normalised output o_c = (sum_r e^{s_r - m_c} v_r) / l_c and
+// lse_c = m_c + log l_c; the merged output is
+//   sum_c e^{lse_c - M} o_c / sum_c e^{lse_c - M},  M = max_c lse_c
+// (the split-KV combine of flash decoding).  Lc lanes (C rounded up to a power
+// of two) share one output, one chunk per lane: one batch of loads, then three
+// group reductions.
+DEV void merge_slice(Ctx& c, const u64* parts, u64* out, int b, int gi, int k0, int n) {
   const StepArgs& a = *c.a;
   const Geom& G = *a.geom;
-  const int b = c.t.a0, g = c.t.a1, ch = c.t.a2;
-  const int D = G.D, NG = G.G, C = G.C, Hkv = G.Hkv, cap = G.cap;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int pos = a.positions[b];
+  const int D = G.D, NG = G.G, C = G.C;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  int Lc = 1;
+  while (Lc < C) Lc <<= 1;
+  const int opw = 64 / Lc, per_pass = NWAVE * opw;
+  const int cl = lane & (Lc - 1);
+  const int cc = cl < C ? cl : C - 1;
+  const size_t cstride = (size_t)NG * (D + 2);
+  const u64* base = parts + (((size_t)b * G.Hkv + gi) * C + cc) * cstride;
+  u64* dst = out + (size_t)b * G.Hq * D + (size_t)gi * NG * D + k0;
+  for (int p = 0; p * per_pass < n; ++p) {
+    const int kk = p * per_pass + wave * opw + lane / Lc;
+    const bool valid = kk < n && cl < C;
+    const int k = k0 + (kk < n ? kk : n - 1);
+    const int h = k / D, d = k - h * D;
+    const u64* pl = base + (size_t)h * (D + 2);
+    const u64 wl = ld_raw(pl), wo = ld_raw(pl + 2 + d);
+    float lse = -INFINITY, o = 0.f;
+    if (valid) {
+      lse = fix_t(wl, pl, a);
+      o = fix_t(wo, pl + 2 + d, a);
+    }
+    const float M = group_reduce<true>(lse, Lc);
+    const float w = lse == -INFINITY ? 0.f : expf(lse - M);
+    const float num = group_reduce<false>(w * o, Lc);
+    const float den = group_reduce<false>(w, Lc);
+    if (valid && cl == 0) st_t(dst + kk, den > 0.f ? num / den : 0.f, a.tag);
+  }
+}
+
+DEV void body_merge(Ctx& c, const OpDesc& op) {
+  merge_slice(c, op.in, op.out, c.t.a0, c.t.a1, c.t.a2, c.t.a3);
+}
+
+// ---------------------------------------------------------------- attention
+// One (sequence b, kv head group gi, chunk ch) task over cache rows
+// [t0, t1) of positions 0..p (p = this step's position of sequence b):
+// q-norm + RoPE for the NG query heads of the group; in the last chunk also
+// k-norm + RoPE of the new key, bf16 rounding and the KV-cache append at p
+// (the new row is used from LDS, not re-read); then scores, the chunk-local
+// softmax (max m, sum l) and the normalised chunk output o / l with
+// lse = m + log l per head.
+// Keys are read 16 bytes per lane (D/8 lanes per row, row sums by DPP);
+// values 4 bytes per lane (D/2 lanes per row), so each lane accumulates its
+// two output columns over whole rows and the only reduction is one pass over
+// the eight wavefronts through LDS.  Both rings are issued before the
+// dependency wait.
+template <int NG, int D>
+DEV void attn_chunk(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int b = c.t.a0, gi = c.t.a1, ch = c.t.a2;
+  const int C = G.C, Hkv = G.Hkv, cap = G.cap;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  constexpr int KL = D / 8, KR = 64 / KL, KP = NWAVE * KR;  // keys: lanes per row, rows per wave, rows per pass
+  constexpr int VL = D / 2, VR = 64 / VL, VP = NWAVE * VR;  // values
+  constexpr int RK = 4, RV = 16;                            // ring depths (passes)
+  int pos = c.pos[b];
   if (pos < 0 || pos >= cap) {
     if (tid == 0) {
       u32 z = 0;
@@ -539,29 +628,33 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
   const int t0 = (int)((long)ch * len / C), t1 = (int)((long)(ch + 1) * len / C);
   const bool last = ch == C - 1;
   const int T = t1 - t0;
-  const int Told = last ? T - 1 : T;  // rows read from the cache (the newest comes from registers)
-  const size_t base = ((((size_t)op.layer * G.B + b) * Hkv + g) * (size_t)cap) * D;
+  const int Told = last ? T - 1 : T;  // rows read from the cache (the newest comes from LDS)
+  const size_t base = ((((size_t)op.layer * G.B + b) * Hkv + gi) * (size_t)cap) * D;
   uint16_t* Kc = a.kv_k + base;
   uint16_t* Vc = a.kv_v + base;
-  const int cpr = D >> 3, rpp = NT / cpr;  // lanes per row, rows per pass
-  const int my_r = tid / cpr, my_c = tid - my_r * cpr;
   const u32 span = (u32)(Told > 0 ? Told : 0) * (u32)D * 2u;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kc + (size_t)t0 * D), 0, (int)span, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vc + (size_t)t0 * D), 0, (int)span, 0x00020000);
-  auto roff = [&](int p) -> u32 {
-    const int r = p * rpp + my_r;
-    return r < Told ? (u32)(r * D + my_c * 8) * 2u : OOB;
+  const int krow = wave * KR + lane / KL, kc = lane % KL;  // key row within a pass, 16-byte column
+  const int vrow = wave * VR + lane / VL, vc = lane % VL;  // value row within a pass, 4-byte column
+  auto koff = [&](int p) -> u32 {
+    const int r = p * KP + krow;
+    return r < Told ? (u32)(r * D + kc * 8) * 2u : OOB;
   };
-  constexpr int RING = 4;
-  u32x4 kr[RING], vr[RING];
+  auto voff = [&](int p) -> u32 {
+    const int r = p * VP + vrow;
+    return r < Told ? (u32)(r * D + vc * 2) * 2u : OOB;
+  };
+  const int nk = (T + KP - 1) / KP, nv = (T + VP - 1) / VP;
+  u32x4 kr[RK];
+  u32 vr[RV];
 #pragma unroll
-  for (int p = 0; p < RING; ++p) {
-    kr[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, roff(p), 0, AUX_NT);
-    vr[p] = __builtin_amdgcn_raw_buffer_load_b128(rv, roff(p), 0, AUX_NT);
-  }
+  for (int p = 0; p < RK; ++p) kr[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff(p), 0, AUX_NT);
+#pragma unroll
+  for (int p = 0; p < RV; ++p) vr[p] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff(p), 0, AUX_NT);
 
   // inputs that do not depend on this step: gains and RoPE frequencies
-  const int half = D >> 1;
+  constexpr int half = D / 2;
   float gq0 = 0.f, gq1 = 0.f, gk0 = 0.f, gk1 = 0.f;
   double ifreq = 0.0;
   if (lane < half) {
@@ -574,16 +667,17 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
 
   wait_dep(c);
 
-  float* qs = (float*)c.lds;                 // [NG][D], pre-scaled by 1/sqrt(D)
-  uint16_t* knew = (uint16_t*)(qs + 8 * 128);  // [D] new key (bf16 bits)
-  uint16_t* vnew = knew + 128;                 // [D] new value
-  float* sc = (float*)(vnew + 128);            // [NG][SMAX] scores, then weights
-  const int SMAX = kScoreFloats / NG;
-  float* red = sc + kScoreFloats;              // [8][NG][D]
-  float* ml = red + 8 * 8 * 128;               // [NG][2]
+  constexpr int SMAX = kScoreFloats / NG;
+  float* qs = (float*)c.lds;                  // [NG][D], pre-scaled by 1/sqrt(D)
+  uint16_t* knew = (uint16_t*)(qs + NG * D);  // [D] new key (bf16 bits)
+  uint16_t* vnew = knew + D;                  // [D] new value
+  float* sc = (float*)(vnew + D);             // [NG][SMAX] raw scores
+  float* pt = sc + kScoreFloats;              // [row][NG] softmax numerators e^{s - m}
+  float* red = pt + kScoreFloats;             // [NWAVE][NG][D] per-wavefront outputs
+  float* ml = red + NWAVE * NG * D;           // [NG][2] m, l
 
   // q / k / v prologue: wavefront h handles head h (then k at NG, v at NG+1)
-  const u64* qkv = op.in + (size_t)b * G.qkv_stride + (size_t)g * (NG + 2) * D;
+  const u64* qkv = op.in + (size_t)b * G.qkv_stride + (size_t)gi * (NG + 2) * D;
   for (int h = wave; h < NG + 2; h += NWAVE) {
     if (h >= NG && !last) continue;
     float x0 = 0.f, x1 = 0.f;
@@ -631,55 +725,53 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
   }
   __syncthreads();
 
-  // scores s[h][r] = q_h . K_r  (q already scaled)
-  const int npass = (T + rpp - 1) / rpp;
-  for (int p0 = 0; p0 < npass; p0 += RING) {
+  // scores s[h][r] = q_h . K_r (q already scaled); this lane's q columns live in registers
+  float q[NG][8];
 #pragma unroll
-    for (int d = 0; d < RING; ++d) {
+  for (int h = 0; h < NG; ++h) {
+    const f32x4 q0 = *(const f32x4*)(qs + h * D + kc * 8);
+    const f32x4 q1 = *(const f32x4*)(qs + h * D + kc * 8 + 4);
+    q[h][0] = q0.x; q[h][1] = q0.y; q[h][2] = q0.z; q[h][3] = q0.w;
+    q[h][4] = q1.x; q[h][5] = q1.y; q[h][6] = q1.z; q[h][7] = q1.w;
+  }
+  for (int p0 = 0; p0 < nk; p0 += RK) {
+#pragma unroll
+    for (int d = 0; d < RK; ++d) {
       const int p = p0 + d;
-      if (p < npass) {
-        const int r = p * rpp + my_r;
+      if (p < nk) {
+        const int r = p * KP + krow;
         u32x4 k = kr[d];
-        if (last && r == T - 1) k = *(const u32x4*)(knew + my_c * 8);
-        float part[8];
+        if (last && r == T - 1) k = *(const u32x4*)(knew + kc * 8);
+        const float kf[8] = {bf_lo(k.x), bf_hi(k.x), bf_lo(k.y), bf_hi(k.y),
+                             bf_lo(k.z), bf_hi(k.z), bf_lo(k.w), bf_hi(k.w)};
+        float s[NG];
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-          part[h] = 0.f;
-          if (h < NG) {
-            const f32x4 q0 = *(const f32x4*)(qs + h * D + my_c * 8);
-            const f32x4 q1 = *(const f32x4*)(qs + h * D + my_c * 8 + 4);
-            float s = bf_lo(k.x) * q0.x;
-            s = fmaf(bf_hi(k.x), q0.y, s);
-            s = fmaf(bf_lo(k.y), q0.z, s);
-            s = fmaf(bf_hi(k.y), q0.w, s);
-            s = fmaf(bf_lo(k.z), q1.x, s);
-            s = fmaf(bf_hi(k.z), q1.y, s);
-            s = fmaf(bf_lo(k.w), q1.z, s);
-            s = fmaf(bf_hi(k.w), q1.w, s);
-            part[h] = s;
-          }
-        }
+        for (int h = 0; h < NG; ++h) {
+          float t = kf[0] * q[h][0];
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-          if (h < NG) {
-            const float s = cpr == 16 ? row16_sum(part[h]) : row8_sum(part[h]);
-            if (my_c == 0 && r < T) sc[h * SMAX + r] = s;
-          }
+          for (int j = 1; j < 8; ++j) t = fmaf(kf[j], q[h][j], t);
+          s[h] = KL == 16 ? row16_sum(t) : row8_sum(t);
         }
+        if (kc == 0 && r < T) {
+#pragma unroll
+          for (int h = 0; h < NG; ++h) sc[h * SMAX + r] = s[h];
+        }
+        if (p + RK < nk) kr[d] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff(p + RK), 0, AUX_NT);
       }
-      kr[d] = __builtin_amdgcn_raw_buffer_load_b128(rk, roff(p + RING), 0, AUX_NT);
     }
   }
   __syncthreads();
-  // chunk-local softmax per head
+
+  // chunk-local softmax per head; numerators to pt[row][h], zero-padded to whole value passes
+  const int Tp = nv * VP;
   for (int h = wave; h < NG; h += NWAVE) {
     float m = -INFINITY;
     for (int r = lane; r < T; r += 64) m = fmaxf(m, sc[h * SMAX + r]);
     m = wave_max(m);
     float l = 0.f;
-    for (int r = lane; r < T; r += 64) {
-      const float e = expf(sc[h * SMAX + r] - m);
-      sc[h * SMAX + r] = e;
+    for (int r = lane; r < Tp; r += 64) {
+      const float e = r < T ? expf(sc[h * SMAX + r] - m) : 0.f;
+      pt[r * NG + h] = e;
       l += e;
     }
     l = wave_sum(l);
@@ -689,135 +781,86 @@ DEV void body_attn(Ctx& c, const OpDesc& op) {
     }
   }
   __syncthreads();
-  // o[h][d] = sum_r w[h][r] V_r[d]
-  float o[8][8];
+
+  // o[h][2 columns] = sum over this lane's rows of p[r][h] V_r
+  float o[NG][2];
 #pragma unroll
-  for (int h = 0; h < 8; ++h)
+  for (int h = 0; h < NG; ++h) o[h][0] = o[h][1] = 0.f;
+  for (int p0 = 0; p0 < nv; p0 += RV) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
-  for (int p0 = 0; p0 < npass; p0 += RING) {
-#pragma unroll
-    for (int d = 0; d < RING; ++d) {
+    for (int d = 0; d < RV; ++d) {
       const int p = p0 + d;
-      if (p < npass) {
-        const int r = p * rpp + my_r;
-        if (r < T) {
-          u32x4 v = vr[d];
-          if (last && r == T - 1) v = *(const u32x4*)(vnew + my_c * 8);
-          const float vv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                               bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+      if (p < nv) {
+        const int r = p * VP + vrow;
+        u32 v = vr[d];
+        if (last && r == T - 1) v = *(const u32*)(vnew + vc * 2);
+        const float v0 = bf_lo(v), v1 = bf_hi(v);
 #pragma unroll
-          for (int h = 0; h < 8; ++h)
-            if (h < NG) {
-              const float w = sc[h * SMAX + r];
-#pragma unroll
-              for (int j = 0; j < 8; ++j) o[h][j] = fmaf(w, vv[j], o[h][j]);
-            }
+        for (int h = 0; h < NG; ++h) {
+          const float w = pt[r * NG + h];
+          o[h][0] = fmaf(w, v0, o[h][0]);
+          o[h][1] = fmaf(w, v1, o[h][1]);
         }
+        if (p + RV < nv) vr[d] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff(p + RV), 0, AUX_NT);
       }
-      vr[d] = __builtin_amdgcn_raw_buffer_load_b128(rv, roff(p + RING), 0, AUX_NT);
     }
   }
-  // reduce over the rows of a pass: lanes that share my_c within the wavefront, then across wavefronts
+  if (VR == 2) {
+    // two rows per wavefront instruction: add the upper half's columns to the lower half
 #pragma unroll
-  for (int h = 0; h < 8; ++h)
-    if (h < NG)
+    for (int h = 0; h < NG; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float s = o[h][j];
-        for (int off = cpr; off < 64; off <<= 1) s += __shfl_xor(s, off);
-        o[h][j] = s;
+      for (int j = 0; j < 2; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[h][j]), __float_as_uint(o[h][j]), false, false);
+        o[h][j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
       }
-  if (lane < cpr) {
+  }
+  if (lane < VL) {
 #pragma unroll
-    for (int h = 0; h < 8; ++h)
-      if (h < NG)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) red[(wave * NG + h) * D + lane * 8 + j] = o[h][j];
+    for (int h = 0; h < NG; ++h) {
+      float* dstp = red + (wave * NG + h) * D + vc * 2;
+      dstp[0] = o[h][0];
+      dstp[1] = o[h][1];
+    }
   }
   __syncthreads();
-  u64* part = op.out + ((((size_t)b * Hkv + g) * C + ch) * NG) * (size_t)(D + 2);
+  u64* part = op.out + ((((size_t)b * Hkv + gi) * C + ch) * NG) * (size_t)(D + 2);
   for (int j = tid; j < NG * D; j += NT) {
     const int h = j / D, dd = j - h * D;
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) s += red[(w * NG + h) * D + dd];
-    st_t(part + (size_t)h * (D + 2) + 2 + dd, s, a.tag);
+    const float l = ml[2 * h + 1];
+    st_t(part + (size_t)h * (D + 2) + 2 + dd, l > 0.f ? s / l : 0.f, a.tag);
   }
   if (tid < NG) {
-    st_t(part + (size_t)tid * (D + 2), ml[2 * tid], a.tag);
-    st_t(part + (size_t)tid * (D + 2) + 1, ml[2 * tid + 1], a.tag);
+    const float m = ml[2 * tid], l = ml[2 * tid + 1];
+    st_t(part + (size_t)tid * (D + 2), l > 0.f ? m + logf(l) : -INFINITY, a.tag);
   }
   if (op.aux) {
     // fused merge: count this chunk's arrival; the last of the C chunks of
-    // (b, g) combines all partials (their words are tagged, so it can read
+    // (b, gi) combines all partials (their words are tagged, so it can read
     // them as soon as they land)
     __syncthreads();
     if (tid == 0) {
-      u32* arr = (u32*)op.aux + ((size_t)b * Hkv + g) * kCounterStride;
+      u32* arr = (u32*)op.aux + ((size_t)b * Hkv + gi) * kCounterStride;
       const u32 old = __hip_atomic_fetch_add(gp(arr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       c.flags[4] = old + 1u == (u32)C * (a.epoch + 1u) ? 1 : 0;
     }
     __syncthreads();
-    if (c.flags[4]) merge_partials(c, op.out, (u64*)op.aux2, b, g);
+    if (c.flags[4]) merge_slice(c, op.out, (u64*)op.aux2, b, gi, 0, NG * D);
   }
 }
 
-// ---------------------------------------------------------------- merge
-// attn[b][g*G+h][d] = sum_c e^{m_c - M} o_c[d] / sum_c e^{m_c - M} l_c
-// Three phases: (m, l) of every (chunk, head) into LDS; per head the max M and
-// the chunk weights e^{m_c - M} (computed once); then every output element
-// fetches its C partial values in one batch.
-//   attn[b][g*G+h][d] = sum_c e^{m_c - M} o_c[d] / sum_c e^{m_c - M} l_c
-DEV void merge_partials(Ctx& c, const u64* parts, u64* out, int b, int g) {
-  const StepArgs& a = *c.a;
-  const Geom& G = *a.geom;
-  const int D = G.D, NG = G.G, C = G.C, tid = threadIdx.x;
-  const u64* part = parts + (((size_t)b * G.Hkv + g) * C) * NG * (size_t)(D + 2);
-  float* wgt = (float*)c.lds + kStageFloats;  // [C][NG]: m, then e^{m - M}
-  float* lsum = wgt + C * NG;                 // [C][NG]: l
-  float* hsum = lsum + C * NG;                // [NG]: sum_c e^{m_c - M} l_c
-  for (int j = tid; j < C * NG; j += NT) {
-    const u64* p = part + (size_t)j * (D + 2);
-    const u64 wm = ld_raw(p), wl = ld_raw(p + 1);
-    wgt[j] = fix_t(wm, p, a);
-    lsum[j] = fix_t(wl, p + 1, a);
-  }
-  __syncthreads();
-  if (tid < NG) {
-    float M = -INFINITY;
-    for (int ch = 0; ch < C; ++ch) M = fmaxf(M, wgt[ch * NG + tid]);
-    float L = 0.f;
-    for (int ch = 0; ch < C; ++ch) {
-      const float m = wgt[ch * NG + tid];
-      const float w = m == -INFINITY ? 0.f : expf(m - M);
-      wgt[ch * NG + tid] = w;
-      L = fmaf(w, lsum[ch * NG + tid], L);
-    }
-    hsum[tid] = L;
-  }
-  __syncthreads();
-  constexpr int CH = 16;
-  for (int j = tid; j < NG * D; j += NT) {
-    const int h = j / D, dd = j - h * D;
-    const u64* p0 = part + (size_t)h * (D + 2) + 2 + dd;
-    const size_t cstride = (size_t)NG * (D + 2);
-    float O = 0.f;
-    for (int c0 = 0; c0 < C; c0 += CH) {
-      u64 w[CH];
-#pragma unroll
-      for (int i = 0; i < CH; ++i) w[i] = ld_raw(p0 + (size_t)min(c0 + i, C - 1) * cstride);
-#pragma unroll
-      for (int i = 0; i < CH; ++i)
-        if (c0 + i < C) {
-          const float wt = wgt[(c0 + i) * NG + h];
-          if (wt != 0.f) O = fmaf(wt, fix_t(w[i], p0 + (size_t)(c0 + i) * cstride, a), O);
-        }
-    }
-    st_t(out + (size_t)b * G.Hq * D + ((size_t)g * NG + h) * D + dd, O / hsum[h], a.tag);
+DEV void body_attn(Ctx& c, const OpDesc& op) {
+  const Geom& G = *c.a->geom;
+  const bool d128 = G.D == 128;
+  switch (G.G) {
+    case 1: d128 ? attn_chunk<1, 128>(c, op) : attn_chunk<1, 64>(c, op); break;
+    case 2: d128 ? attn_chunk<2, 128>(c, op) : attn_chunk<2, 64>(c, op); break;
+    case 4: d128 ? attn_chunk<4, 128>(c, op) : attn_chunk<4, 64>(c, op); break;
+    default: d128 ? attn_chunk<8, 128>(c, op) : attn_chunk<8, 64>(c, op); break;
   }
 }
-
-DEV void body_merge(Ctx& c, const OpDesc& op) { merge_partials(c, op.in, op.out, c.t.a0, c.t.a1); }
 
 }  // namespace mk

@@ -151,9 +151,9 @@ void build_decoder_ops(Graph& g) {
       }
     }
     // Attention chunks: (b, g, chunk); the last chunk appends the new k/v.
-    // Without merge tasks the op is joint: the last chunk of (b, g) to finish
-    // reads every chunk's partial and writes the merged heads.
-    const bool fused = g.opts.merge_tasks == 0;
+    // With merge_tasks == 2 the op is joint: the last chunk of (b, g) to
+    // finish reads every chunk's partial and writes the merged heads.
+    const bool fused = g.opts.merge_tasks == 2;
     {
       int32_t o = bd.op(OP_ATTN, l, D, 0, 0);
       g.ops[o].in_buf = qkv;
@@ -177,15 +177,19 @@ void build_decoder_ops(Graph& g) {
           }
     }
     if (!fused) {
+      // merge tasks: S slices of the G*D outputs of each (b, g), each slice
+      // combining the C partials of its outputs (S = 1: one task per group)
+      const int32_t S = g.merge_slices;
       int32_t o = bd.op(OP_MERGE, l, D, 0, 0);
       g.ops[o].in_buf = part;
       g.ops[o].out_buf = attn;
       for (int32_t b = 0; b < B; ++b)
-        for (int32_t gi = 0; gi < Hkv; ++gi) {
-          RawTask& t = bd.task(o, b, gi);
-          Builder::rd(t, part, ((int64_t)b * Hkv + gi) * C * PW, (int64_t)C * PW);
-          Builder::wr(t, attn, (int64_t)b * Hq * D + (int64_t)gi * G * D, (int64_t)G * D);
-        }
+        for (int32_t gi = 0; gi < Hkv; ++gi)
+          for (auto rr : split_rows(G * D, S, 1)) {
+            RawTask& t = bd.task(o, b, gi, rr.first, rr.second);
+            Builder::rd(t, part, ((int64_t)b * Hkv + gi) * C * PW, (int64_t)C * PW);
+            Builder::wr(t, attn, (int64_t)b * Hq * D + (int64_t)gi * G * D + rr.first, rr.second);
+          }
     }
     {
       int32_t o = bd.op(OP_OPROJ, l, Hq * D, H, 0);
@@ -929,7 +933,12 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
     return bad("shape fields must be positive");
   if (s.n_q_heads % s.n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
   if (s.head_dim % 64 || s.head_dim > 128) return bad("head_dim must be 64 or 128");
-  if (s.n_q_heads / s.n_kv_heads > 8) return bad("at most 8 query heads per kv head");
+  {
+    const int32_t gq = s.n_q_heads / s.n_kv_heads;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8) return bad("query heads per kv head must be 1, 2, 4 or 8");
+  }
+  if (o.merge_tasks < 0 || o.merge_tasks > 2) return bad("merge_tasks must be 0, 1 or 2");
+  if (o.attn_chunks > 64) return bad("attn_chunks must be <= 64");
   if (s.hidden % 64) return bad("hidden must be a multiple of 64");
   if (s.n_experts == 0 && (s.intermediate <= 0 || s.intermediate % 16)) return bad("intermediate must be a positive multiple of 16");
   if (s.n_experts > 0 && (s.top_k <= 0 || s.top_k > s.n_experts || s.top_k > 8 || s.expert_intermediate % 16 ||
@@ -978,13 +987,18 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   const int32_t bh = batch * s.n_kv_heads;
   int32_t C = o.attn_chunks;
   if (C <= 0) C = std::max(1, std::min(workers / std::max(1, bh), std::max(1, cap / 32)));
-  // the scores of one chunk (G heads x chunk length) must fit the LDS score area
-  {
-    const int64_t G = s.n_q_heads / s.n_kv_heads;
-    while ((int64_t)G * ((cap + C - 1) / C + 1) > kScoreFloats) ++C;
+  // the scores of one chunk (G heads x chunk length, padded to whole value
+  // passes of 16 rows) must fit the LDS score area
+  const int64_t Gq = s.n_q_heads / s.n_kv_heads;
+  while (Gq * ((cap + C - 1) / C + 16) > kScoreFloats) ++C;
+  // the merge gives each chunk one lane of a wavefront
+  if (C > 64) {
+    delete g;
+    return bad("attention needs more than 64 chunks per (sequence, kv head) for this context; reduce max_ctx");
   }
-  // the merge keeps 2 floats per (chunk, head) in a 32 KB LDS area
-  g->C = std::min(C, std::max(1, (kRowResultFloats - 16) / (2 * (s.n_q_heads / s.n_kv_heads))));
+  g->C = C;
+  if (o.merge_tasks == 1) g->merge_slices = 1;
+  else g->merge_slices = (int32_t)std::max<int64_t>(1, std::min<int64_t>(C, Gq * s.head_dim / 16));
   build_decoder_ops(*g);
   if (!finish_graph(*g, err)) {
     delete g;

@@ -56,6 +56,7 @@ struct Graph {
   mk_build_opts opts{};
   int32_t W = 0;        // workers
   int32_t C = 0;        // attention chunks per (sequence, kv head)
+  int32_t merge_slices = 1;  // merge tasks per (sequence, kv head)
   int32_t gemv = 0;     // MK_GEMV_VALU or MK_GEMV_MFMA
   int32_t granule = 1;  // GEMV tile row granule
   bool fuse = true;     // event fusion (off only for compiler tests)

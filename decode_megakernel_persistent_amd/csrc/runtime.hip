@@ -29,7 +29,7 @@ namespace mk {
 
 // ---------------------------------------------------------------- kernels
 template <int NB>
-DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int* flags) {
+DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int* flags, const int* pos) {
   Ctx c;
   c.a = &a;
   c.t = a.tasks[id];
@@ -38,6 +38,7 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
   c.lpt = lpt;
   c.lds = lds;
   c.flags = flags;
+  c.pos = pos;
   const OpDesc& op = a.ops[c.t.op];
   switch (op.kind) {
     case OP_QKV:
@@ -66,7 +67,10 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
   finish(c);
 }
 
-DEV bool entry_ok(const StepArgs& a, int* flags) {
+// Entry checks of every worker / launch; also copies the step's positions
+// (at most 16) into LDS, so that no task pays a memory round trip for them.
+DEV bool entry_ok(const StepArgs& a, int* flags, int* pos) {
+  if ((int)threadIdx.x < a.geom->B) pos[threadIdx.x] = a.positions[threadIdx.x];
   if (threadIdx.x == 0) {
     int ok = 1;
     if (a.geom->magic != a.magic) {
@@ -90,13 +94,14 @@ template <int NB>
 __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerVgprs))) mk_worker(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flags[64];
+  __shared__ int pos[16];
   if (threadIdx.x == 0) __hip_atomic_fetch_add(a.status + ST_ARRIVED, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (entry_ok(a, flags)) {
+  if (entry_ok(a, flags, pos)) {
     const int w = blockIdx.x;
     for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
       if (threadIdx.x == 0)
         __hip_atomic_store(a.progress + w, (u32)a.wl_ids[k] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      run_task<NB>(a, a.wl_ids[k], w, false, lds, flags);
+      run_task<NB>(a, a.wl_ids[k], w, false, lds, flags, pos);
       __syncthreads();
       if (flags[0]) break;
     }
@@ -110,7 +115,8 @@ template <int NB>
 __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flags[64];
-  if (entry_ok(a, flags)) run_task<NB>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags);
+  __shared__ int pos[16];
+  if (entry_ok(a, flags, pos)) run_task<NB>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags, pos);
 }
 
 // The dispatch wavefront: runs the dispatcher's own task list (work-list

@@ -88,8 +88,10 @@ typedef struct {
   int32_t spin_timeout_us; /* watchdog budget of any single device wait; 0 = 2 s */
   int32_t no_fusion;       /* 1 = one event per dependency edge (analysis only: normalisation then
                               inserts empty tasks); 0 = fuse events (default) */
-  int32_t merge_tasks;     /* 1 = separate attention-merge tasks; 0 = the last chunk of each
-                              (sequence, kv head) to finish merges the partials (default) */
+  int32_t merge_tasks;     /* how the attention chunks' partials are combined: 0 = merge tasks, each
+                              combining one slice of a (sequence, kv head)'s outputs (default);
+                              1 = one merge task per (sequence, kv head); 2 = no merge tasks: the
+                              last chunk of each (sequence, kv head) to finish merges them */
   int32_t no_watchdog;     /* 1 = persistent mode launches no dispatch wavefront (no residency
                               handshake, no step watchdog; the workers' own bounded waits remain).
                               For profilers that serialise kernel dispatches.  Rejected with

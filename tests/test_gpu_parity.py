@@ -79,9 +79,11 @@ def test_tiny_small_worker_count(tiny):
     assert_reports(reports)
 
 
-def test_tiny_separate_merge_tasks(tiny):
+@pytest.mark.parametrize("merge_tasks", [1, 2])
+def test_tiny_merge_variants(tiny, merge_tasks):
+    # 1: one merge task per (sequence, kv head); 2: the last chunk merges
     w, prep = tiny
-    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=3, merge_tasks=1)
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=3, merge_tasks=merge_tasks)
     assert_reports(reports)
 
 

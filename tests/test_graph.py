@@ -74,6 +74,8 @@ def ancestors_matrix(tasks, ev):
 @pytest.mark.parametrize("shape,batch,kw", [
     (TINY.shape, 1, {}),
     (TINY.shape, 1, {"merge_tasks": 1}),
+    (TINY.shape, 1, {"merge_tasks": 2}),
+    (SMALL, 1, {"num_workers": 64}),
     (TINY.shape, 3, {"attn_chunks": 3}),
     (SMALL, 2, {"num_workers": 7}),
     (MOE, 2, {"num_workers": 8}),
@@ -128,19 +130,20 @@ def test_head_group_aligned_qkv_tiles():
         mk.mk_destroy_graph(g)
 
 
-@pytest.mark.parametrize("merge_tasks", [0, 1])
-def test_8b_graph_shape_counts(merge_tasks):
+@pytest.mark.parametrize("merge_tasks,merges,merge_events", [(0, 256, 8), (1, 8, 8), (2, 0, 0)])
+def test_8b_graph_shape_counts(merge_tasks, merges, merge_events):
     s = synth.WORKLOADS["qwen3-8b"]
     g = mk.mk_build_graph(s.shape, 1, s.capacity, mk.make_opts(num_workers=256, merge_tasks=merge_tasks))
     try:
         st = mk.mk_graph_stats(g)
-        # per layer: 256 QKV + 256 attention chunks (+ 8 merges) + 256 O + 256 gate-up + 256 down
-        assert st.tasks == 1 + 36 * (256 * 5 + 8 * merge_tasks) + 256
+        assert st.attn_chunks == 32
+        # per layer: 256 QKV + 256 attention chunks + merges + 256 O + 256 gate-up + 256 down
+        assert st.tasks == 1 + 36 * (256 * 5 + merges) + 256
         assert st.empty_tasks == 0
-        # per layer: QKV, 8 head groups, (8 merges), O, gate-up, down
-        assert st.events == 36 * (12 + 8 * merge_tasks) + 1
+        # per layer: 8 QKV head groups, (8 chunk groups), attention/merge -> O, O, gate-up, down
+        assert st.events == 36 * (12 + merge_events) + 1
         assert st.launches_per_step == st.events + 1
-        assert st.max_tasks_per_worker <= 36 * 6 + 2
+        assert st.max_tasks_per_worker <= 36 * (5 + (merges + 255) // 256) + 2
         assert abs(st.weight_bytes / 1e9 - 15.137) < 0.01
     finally:
         mk.mk_destroy_graph(g)
