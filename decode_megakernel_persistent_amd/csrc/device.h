@@ -324,14 +324,32 @@ DEV void body_embed(Ctx& c, const OpDesc& op) {
 }
 
 // ---------------------------------------------------------------- GEMV input staging
-// xs[b][k] = in[b][k], or rmsnorm(in[b]) * g when the op normalises its input.
+// xs[b][k] = in[b][k] * g[k] (g = 1 when the op does not normalise its input),
+// ss[b] = this thread's part of sum_k in[b][k]^2.  The RMSNorm scale
+// rsqrt(mean(in^2) + eps) is a per-sequence scalar, so it is applied to the
+// dot products in the epilogue instead of rescaling xs.
+// Staging runs in two parts so that the first batch of input words can be
+// issued ahead of the rest of the weight ring: in-order load completion would
+// otherwise make the input wait behind the whole ring.
+constexpr int kStageCH = 8;  // tagged words in flight per thread
+struct StageFirst {
+  u64 w[kStageCH];
+  float g[kStageCH];
+};
+
+DEV void stage_issue(const OpDesc& op, int tid, StageFirst& f) {
+  const int K = op.K;
+#pragma unroll
+  for (int i = 0; i < kStageCH; ++i) f.w[i] = ld_raw(op.in + min(tid + i * NT, K - 1));
+#pragma unroll
+  for (int i = 0; i < kStageCH; ++i) f.g[i] = op.norm_in ? ldg(op.g + min(tid + i * NT, K - 1)) : 1.0f;
+}
+
 template <int NB>
-DEV void stage_input(Ctx& c, const OpDesc& op, float* xs, float* red) {
+DEV void stage_finish(Ctx& c, const OpDesc& op, int tid, const StageFirst& f, float* xs, float (&ss)[NB]) {
   const StepArgs& a = *c.a;
-  const int K = op.K, tid = task_tid();
-  constexpr int CH = 8;  // tagged words in flight per thread
-  const bool nrm = op.norm_in != 0;
-  float ss[NB];
+  const int K = op.K;
+  constexpr int CH = kStageCH;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     ss[b] = 0.f;
@@ -339,19 +357,18 @@ DEV void stage_input(Ctx& c, const OpDesc& op, float* xs, float* red) {
     for (int k0 = 0; k0 < K; k0 += NT * CH) {
       u64 w[CH];
       float gv[CH];
-      // unconditional loads (clamped index) so that all of them are in
-      // flight before the first tag check
+      if (b == 0 && k0 == 0) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int k = min(k0 + tid + i * NT, K - 1);
-        w[i] = ld_raw(in + k);
-      }
-      if (nrm) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) gv[i] = ldg(op.g + min(k0 + tid + i * NT, K - 1));
+        for (int i = 0; i < CH; ++i) {
+          w[i] = f.w[i];
+          gv[i] = f.g[i];
+        }
       } else {
+        // unconditional loads (clamped index): all in flight before the first tag check
 #pragma unroll
-        for (int i = 0; i < CH; ++i) gv[i] = 1.0f;
+        for (int i = 0; i < CH; ++i) w[i] = ld_raw(in + min(k0 + tid + i * NT, K - 1));
+#pragma unroll
+        for (int i = 0; i < CH; ++i) gv[i] = op.norm_in ? ldg(op.g + min(k0 + tid + i * NT, K - 1)) : 1.0f;
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -364,16 +381,9 @@ DEV void stage_input(Ctx& c, const OpDesc& op, float* xs, float* red) {
       }
     }
   }
-  if (nrm) {
-    block_sum<NB>(ss, red);
-    const float eps = a.geom->eps;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float r = rsqrtf(ss[b] / (float)K + eps);
-      for (int k = tid; k < K; k += NT) xs[b * K + k] *= r;
-    }
-  }
 }
+
+DEV float a_eps(const Ctx& c) { return c.a->geom->eps; }
 
 // ---------------------------------------------------------------- GEMV epilogue
 // Residual words of this thread's first epilogue output, loaded right after
@@ -386,12 +396,13 @@ DEV u64 gemv_residual_prefetch(const Ctx& c, const OpDesc& op, int NB) {
 }
 
 template <int NB>
-DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 res0) {
+DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 res0, const float* rn) {
   const StepArgs& a = *c.a;
   const int nr = c.t.a2, r0 = c.t.a1, N = op.N;
   for (int j = threadIdx.x; j < NB * nr; j += NT) {
     const int b = j / nr, r = j - b * nr, row = r0 + r;
-    const float v = rsl[b * NR + r];
+    const float scale = rn[b];
+    const float v = rsl[b * NR + r] * scale;
     switch (op.kind) {
       case OP_QKV:
       case OP_ROUTER:
@@ -405,7 +416,7 @@ DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 r
         break;
       }
       case OP_GATEUP:
-        st_t(op.out + (size_t)b * N + row, silu(v) * rsl[b * NR + nr + r], a.tag);
+        st_t(op.out + (size_t)b * N + row, silu(v) * (rsl[b * NR + nr + r] * scale), a.tag);
         break;
       case OP_LMHEAD:
         a.logits[(size_t)b * N + row] = v;
@@ -420,13 +431,14 @@ DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 r
 // Tile = NR contiguous bf16 rows of length K.  Wavefront w owns rows w, w+8, ...;
 // in each row lane l reads 16-byte chunks l, l+64, ... (1 KB coalesced per
 // wavefront load).  A row is cut into segments of S chunks per lane; a ring of
-// DEPTH segments keeps about 32 loads per lane in flight, and the first DEPTH
-// segments are issued before the dependency wait.  Loads go through a buffer
-// resource so out-of-range segments return zeros without touching memory.
+// DEPTH segments keeps LOADS loads per lane in flight.  Before the dependency
+// wait only the first op.pre loads are issued; after it the first batch of
+// input words goes out, then the rest of the ring, then the input is staged
+// while the ring streams.  Loads go through a buffer resource so that
+// out-of-range segments return zeros without touching memory.
 template <int NB, int S>
 DEV void gemv_valu(Ctx& c, const OpDesc& op) {
-  // about 28 loads in flight per lane (24 when 3-4 sequences need more accumulators)
-  constexpr int LOADS = NB <= 2 ? 28 : 24;
+  constexpr int LOADS = 8;
   constexpr int DEPTH = LOADS / S > 1 ? LOADS / S : 2;
   const Task& t = c.t;
   const int K = op.K, CPR = K >> 3, NCH = (CPR + 63) >> 6, SPR = NCH / S;
@@ -435,6 +447,7 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
   const int nrw = NR > wave ? (NR - wave + NWAVE - 1) / NWAVE : 0;
   const int NSEG = nrw * SPR;
+  const int PRE = min(DEPTH, (op.pre + S - 1) / S);  // ring segments issued before the wait
   const uint16_t* Wt = op.w + (size_t)(u32)t.a3;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, (int)((u32)NR * (u32)K * 2u), 0x00020000);
@@ -449,18 +462,47 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
+    if (d < PRE) {
 #pragma unroll
-    for (int u = 0; u < S; ++u) buf[d][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff(fi, fq, u), 0, AUX_NT);
-    if (++fq == SPR) { fq = 0; ++fi; }
+      for (int u = 0; u < S; ++u) buf[d][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff(fi, fq, u), 0, AUX_NT);
+      if (++fq == SPR) { fq = 0; ++fi; }
+    }
   }
 
   wait_dep(c);
   float* xs = (float*)c.lds;
   float* rsl = xs + kStageFloats;
   float* red = (float*)(c.flags + 8);
+  StageFirst sf;
+  stage_issue(op, tid, sf);
   const u64 res0 = gemv_residual_prefetch(c, op, NB);
-  stage_input<NB>(c, op, xs, red);
-  __syncthreads();
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    if (d >= PRE) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) buf[d][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff(fi, fq, u), 0, AUX_NT);
+      if (++fq == SPR) { fq = 0; ++fi; }
+    }
+  }
+  float ss[NB];
+  stage_finish<NB>(c, op, tid, sf, xs, ss);
+  // per-sequence RMSNorm scale of the input (1 when the op has no input
+  // norm), kept in LDS next to the reduction slots for the epilogue; the
+  // block reduction's barriers also publish xs for the loop
+  float* rn = red + NB * NWAVE;
+  if (op.norm_in) {
+    block_sum<NB>(ss, red);
+    if (tid < NB) {
+      float v = ss[0];
+#pragma unroll
+      for (int b = 1; b < NB; ++b)
+        if (tid == b) v = ss[b];
+      rn[tid] = rsqrtf(v / (float)K + a_eps(c));
+    }
+  } else {
+    if (tid < NB) rn[tid] = 1.0f;
+    __syncthreads();
+  }
 
   float acc[NB];
 #pragma unroll
@@ -509,7 +551,7 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
     }
   }
   __syncthreads();
-  gemv_epilogue<NB>(c, op, rsl, NR, res0);
+  gemv_epilogue<NB>(c, op, rsl, NR, res0, rn);
 }
 
 template <int NB>

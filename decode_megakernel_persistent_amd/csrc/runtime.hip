@@ -284,6 +284,15 @@ mk_status mk_workspace_size(const mk_graph* g, size_t* arena_bytes, size_t* scra
   return MK_OK;
 }
 
+// GEMV weight loads per lane issued before the dependency wait.  A load
+// issue blocks once the compute unit's outstanding-miss capacity is full, so
+// a deep pre-wait burst delays the wait and the input staging behind data
+// that then sits in registers; a short burst lets staging overlap the stream.
+static int32_t default_prefetch_loads(int32_t kind) {
+  (void)kind;
+  return 64;  // the whole ring
+}
+
 mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void* d_arena, void* d_scratch,
                           void* d_trace, void* stream_) {
   if (!g || !g->G || (!tensors && n > 0) || !d_arena || !d_scratch) {
@@ -395,6 +404,7 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
     d.N = o.N;
     d.norm_in = o.norm_in;
     d.ntasks = o.ntasks;
+    d.pre = G.opts.prefetch_loads > 0 ? G.opts.prefetch_loads : default_prefetch_loads(o.kind);
     d.w = o.w_off >= 0 ? (const uint16_t*)(arena + o.w_off) : nullptr;
     d.g = o.g_off >= 0 ? (const float*)(arena + o.g_off) : nullptr;
     d.g2 = o.g2_off >= 0 ? (const float*)(arena + o.g2_off) : nullptr;

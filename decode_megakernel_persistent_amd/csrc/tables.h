@@ -60,7 +60,8 @@ struct OpDesc {
   int32_t N;         // GEMV output length per sequence
   int32_t norm_in;   // 1: input is rmsnorm(in) * g
   int32_t ntasks;
-  int32_t pad[2];
+  int32_t pre;       // GEMV: weight loads per lane issued before the dependency wait
+  int32_t pad;
   const uint16_t* w; // weight block (bf16)
   const float* g;    // input-norm gain [K] (or q-norm gain [D])
   const float* g2;   // k-norm gain [D]

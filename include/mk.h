@@ -96,7 +96,9 @@ typedef struct {
                               handshake, no step watchdog; the workers' own bounded waits remain).
                               For profilers that serialise kernel dispatches.  Rejected with
                               MK_ERR_ARG when the graph has dispatcher tasks (routed experts). */
-  int32_t reserved[6];     /* must be zero */
+  int32_t prefetch_loads;  /* GEMV weight loads per lane (16 bytes each) issued before a task's
+                              dependency wait; 0 = per-operator default */
+  int32_t reserved[5];     /* must be zero */
 } mk_build_opts;
 
 /* One logical tensor handed to mk_load_weights.  Names:
