@@ -191,9 +191,8 @@ DEV u32 event_total(const StepArgs& a, int ev, int lane) {
   if (lane < kSubCounters)
     v = __hip_atomic_load(gp(a.counters + ((size_t)ev * kSubCounters + lane) * kCounterStride), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
+#pragma unroll
+  for (int o = 1; o < kSubCounters; o <<= 1) v += __shfl_xor(v, o);
   return (u32)__builtin_amdgcn_readlane((int)v, 0);
 }
 
@@ -211,13 +210,13 @@ DEV void report_timeout(const StepArgs& a, int task, int ev, u32 seen, u32 targe
   __hip_atomic_store(a.status + ST_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait for the task's dependency event (wavefront 0 polls, the others wait at
-// the barrier), then take the trace start ticket.  All threads call this.
-DEV void wait_dep(Ctx& c) {
+// Wavefront 0 only: poll the task's dependency event until it reaches its
+// target (bounded by the watchdog budget), then take the trace start ticket.
+DEV void poll_dep(Ctx& c) {
   const StepArgs& a = *c.a;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = threadIdx.x & 63;
   const int ev = c.t.dep;
-  if (tid < 64) {
+  {
     u32 seen = 0;
     int bad = 0;
     if (ev >= 0) {
@@ -244,11 +243,19 @@ DEV void wait_dep(Ctx& c) {
       c.flags[1] = (int)seen;
       if (bad) c.flags[0] = 1;
       if (a.trace_on) {
-        c.flags[2] = (int)__hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        c.flags[2] = a.trace_on == 1
+                         ? (int)__hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0;
         c.flags[3] = (int)(u32)wall_clock64();
       }
     }
   }
+}
+
+// Wait for the task's dependency event (wavefront 0 polls, the others wait at
+// the barrier).  All threads call this.
+DEV void wait_dep(Ctx& c) {
+  if (threadIdx.x < 64) poll_dep(c);
   __syncthreads();
 }
 
@@ -261,8 +268,12 @@ DEV void finish(Ctx& c) {
   __syncthreads();
   if (threadIdx.x == 0) {
     if (a.trace_on && !c.flags[0]) {
-      u32 te = __hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      u32 slot = __hip_atomic_fetch_add(a.status + ST_TRACE_N, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // ticketed trace: global tickets and append order; timing trace: clocks
+      // only, one slot per task id (no returning atomics on the task's path)
+      const bool tk = a.trace_on == 1;
+      u32 te = tk ? __hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      u32 slot = tk ? __hip_atomic_fetch_add(a.status + ST_TRACE_N, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : (u32)c.id;
       if (slot < (u32)a.geom->n_tasks) {
         mk_trace_rec r;
         r.task = c.id;
@@ -385,6 +396,24 @@ DEV void stage_finish(Ctx& c, const OpDesc& op, int tid, const StageFirst& f, fl
 
 DEV float a_eps(const Ctx& c) { return c.a->geom->eps; }
 
+// Old-path norm: block reduction of the per-thread sums into rn (its barriers
+// also publish xs).
+template <int NB>
+DEV void stage_norm(Ctx& c, const OpDesc& op, int tid, float (&ss)[NB], float* red, float* rn) {
+  if (op.norm_in) {
+    block_sum<NB>(ss, red);
+    if (tid < NB) {
+      float v = ss[0];
+#pragma unroll
+      for (int b = 1; b < NB; ++b)
+        if (tid == b) v = ss[b];
+      rn[tid] = rsqrtf(v / (float)op.K + a_eps(c));
+    }
+  } else {
+    if (tid < NB) rn[tid] = 1.0f;
+  }
+}
+
 // ---------------------------------------------------------------- GEMV epilogue
 // Residual words of this thread's first epilogue output, loaded right after
 // the wait so that the load overlaps the weight stream.
@@ -436,9 +465,8 @@ DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 r
 // input words goes out, then the rest of the ring, then the input is staged
 // while the ring streams.  Loads go through a buffer resource so that
 // out-of-range segments return zeros without touching memory.
-template <int NB, int S>
+template <int NB, int S, int LOADS>
 DEV void gemv_valu(Ctx& c, const OpDesc& op) {
-  constexpr int LOADS = 8;
   constexpr int DEPTH = LOADS / S > 1 ? LOADS / S : 2;
   const Task& t = c.t;
   const int K = op.K, CPR = K >> 3, NCH = (CPR + 63) >> 6, SPR = NCH / S;
@@ -460,6 +488,12 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
     if (i >= nrw || cc >= CPR) return OOB;
     return (u32)((wave + NWAVE * i) * K + cc * 8) * 2u;
   };
+  float* xs = (float*)c.lds;
+  float* rsl = xs + kStageFloats;
+  float* red = (float*)(c.flags + 8);
+  // per-sequence RMSNorm scale of the input (1 when the op has no input
+  // norm), kept in LDS next to the reduction slots for the epilogue
+  float* rn = red + NB * NWAVE;
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     if (d < PRE) {
@@ -468,14 +502,9 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
       if (++fq == SPR) { fq = 0; ++fi; }
     }
   }
-
   wait_dep(c);
-  float* xs = (float*)c.lds;
-  float* rsl = xs + kStageFloats;
-  float* red = (float*)(c.flags + 8);
   StageFirst sf;
   stage_issue(op, tid, sf);
-  const u64 res0 = gemv_residual_prefetch(c, op, NB);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     if (d >= PRE) {
@@ -486,23 +515,9 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   }
   float ss[NB];
   stage_finish<NB>(c, op, tid, sf, xs, ss);
-  // per-sequence RMSNorm scale of the input (1 when the op has no input
-  // norm), kept in LDS next to the reduction slots for the epilogue; the
-  // block reduction's barriers also publish xs for the loop
-  float* rn = red + NB * NWAVE;
-  if (op.norm_in) {
-    block_sum<NB>(ss, red);
-    if (tid < NB) {
-      float v = ss[0];
-#pragma unroll
-      for (int b = 1; b < NB; ++b)
-        if (tid == b) v = ss[b];
-      rn[tid] = rsqrtf(v / (float)K + a_eps(c));
-    }
-  } else {
-    if (tid < NB) rn[tid] = 1.0f;
-    __syncthreads();
-  }
+  stage_norm<NB>(c, op, tid, ss, red, rn);
+  __syncthreads();
+  const u64 res0 = gemv_residual_prefetch(c, op, NB);
 
   float acc[NB];
 #pragma unroll
@@ -554,14 +569,24 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   gemv_epilogue<NB>(c, op, rsl, NR, res0, rn);
 }
 
+// Ring depth (loads per lane).  Deeper rings, also for the O projection that
+// waits through attention and the merge, measured slower: the extra traffic
+// lengthens the latency-bound attention -> merge -> O chain more than the
+// prefetch saves.
+constexpr int kRingDeep = 8, kRingShallow = 8;
+template <int NB, int LOADS>
+DEV void gemv_valu_s(Ctx& c, const OpDesc& op) {
+  const int nch = ((op.K >> 3) + 63) >> 6;
+  if (nch % 4 == 0) gemv_valu<NB, 4, LOADS>(c, op);
+  else if (nch % 6 == 0) gemv_valu<NB, 6, LOADS>(c, op);
+  else if (nch % 3 == 0) gemv_valu<NB, 3, LOADS>(c, op);
+  else if (nch % 2 == 0) gemv_valu<NB, 2, LOADS>(c, op);
+  else gemv_valu<NB, 1, LOADS>(c, op);
+}
 template <int NB>
 DEV void gemv_valu_any(Ctx& c, const OpDesc& op) {
-  const int nch = ((op.K >> 3) + 63) >> 6;
-  if (nch % 4 == 0) gemv_valu<NB, 4>(c, op);
-  else if (nch % 6 == 0) gemv_valu<NB, 6>(c, op);
-  else if (nch % 3 == 0) gemv_valu<NB, 3>(c, op);
-  else if (nch % 2 == 0) gemv_valu<NB, 2>(c, op);
-  else gemv_valu<NB, 1>(c, op);
+  if (op.kind == OP_OPROJ) gemv_valu_s<NB, kRingDeep>(c, op);
+  else gemv_valu_s<NB, kRingShallow>(c, op);
 }
 
 // ---------------------------------------------------------------- group reductions

@@ -950,6 +950,7 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   for (int i = 0; i < 5; ++i)
     if (o.reserved[i]) return bad("reserved options must be zero");
   if (o.prefetch_loads < 0 || o.prefetch_loads > 64) return bad("prefetch_loads must be in 0..64");
+  if (o.trace < 0 || o.trace > 2) return bad("trace must be 0, 1 or 2");
   if (o.no_watchdog && s.n_experts > 0) return bad("no_watchdog: routed-expert graphs need the dispatch wavefront");
 
   Graph* g = new Graph();

@@ -513,10 +513,10 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
   a.epoch = g->epoch;
   a.tag = g->tag;
   a.magic = G.geom.magic;
-  a.trace_on = G.opts.trace ? 1 : 0;
+  a.trace_on = G.opts.trace;
   a.n_workers = G.W;
   const int nb = G.B;
-  if (a.trace_on) HIPCHK(hipMemsetAsync(a.status + ST_TICKET, 0, 2 * sizeof(u32), stream));
+  if (a.trace_on == 1) HIPCHK(hipMemsetAsync(a.status + ST_TICKET, 0, 2 * sizeof(u32), stream));
   if (g->mode == MK_PERSISTENT) {
     hipStream_t side = (hipStream_t)g->side_stream;
     const bool watch = !G.opts.no_watchdog;
@@ -657,8 +657,9 @@ mk_status mk_read_trace(mk_graph* g, mk_trace_rec* host_buf, int64_t cap, int64_
     set_error("mk_read_trace: graph built without trace");
     return MK_ERR_STATE;
   }
-  u32 cnt = 0;
-  HIPCHK(hipMemcpy(&cnt, (char*)g->scratch + G.off_status + ST_TRACE_N * 4, 4, hipMemcpyDeviceToHost));
+  u32 cnt = (u32)G.tasks.size();  // timing trace: one slot per task
+  if (G.opts.trace == 1)
+    HIPCHK(hipMemcpy(&cnt, (char*)g->scratch + G.off_status + ST_TRACE_N * 4, 4, hipMemcpyDeviceToHost));
   int64_t m = std::min<int64_t>({(int64_t)cnt, cap, (int64_t)G.tasks.size()});
   if (m > 0 && host_buf) HIPCHK(hipMemcpy(host_buf, g->trace, (size_t)m * sizeof(mk_trace_rec), hipMemcpyDeviceToHost));
   *n = (int64_t)cnt;

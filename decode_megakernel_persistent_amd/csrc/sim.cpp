@@ -206,6 +206,10 @@ mk_status mk_check_trace(const mk_graph* g, const mk_trace_rec* recs, int64_t n,
     mk::set_error("mk_check_trace: null argument");
     return MK_ERR_ARG;
   }
+  if (g->G->opts.trace == 2) {
+    mk::set_error("mk_check_trace: a timing trace (trace = 2) carries no tickets; build with trace = 1");
+    return MK_ERR_ARG;
+  }
   std::string err;
   // `step` is the epoch of the traced step; counters are totals after it
   if (!mk::check_trace(*g->G, recs, n, step, counters, step + 1, &err)) {

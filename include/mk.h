@@ -82,7 +82,9 @@ typedef struct {
   int32_t mode;            /* MK_PERSISTENT or MK_LAUNCH_PER_TASK (mk_set_mode can switch) */
   int32_t per_task_launch; /* launch-per-task only: 1 = one launch per task (stress mode) */
   int32_t num_workers;     /* 0 = the device's compute-unit count */
-  int32_t trace;           /* 1 = record one mk_trace_rec per executed task */
+  int32_t trace;           /* 1 = record one mk_trace_rec per executed task (global tickets, for
+                              mk_check_trace); 2 = timing trace: clocks only, record i = task i,
+                              no atomics on the task's path (tickets are 0); 0 = off */
   int32_t attn_chunks;     /* attention chunks per (sequence, kv head); 0 = auto */
   int32_t gemv;            /* MK_GEMV_* */
   int32_t spin_timeout_us; /* watchdog budget of any single device wait; 0 = 2 s */

@@ -40,7 +40,15 @@ def run_steps(w, prep, mode, steps, trace=True, workers=0, gemv=mk.MK_GEMV_AUTO,
             lg_o = orc.decode(tok, pos)
             rep = harness.compare(lg_g, lg_o)
             reports.append(rep)
-            if trace:
+            if trace == 2:
+                # timing trace: record i is task i, stamped by a worker, clocks ordered
+                recs = sess.read_trace()
+                np.testing.assert_array_equal(recs["task"], np.arange(len(recs)))
+                assert recs["worker"].min() >= 0 and recs["worker"].max() < sess.stats.workers
+                assert np.all(recs["step"] == recs["step"][0])
+                dt = (recs["clk_end"].astype(np.int64) - recs["clk_start"].astype(np.int64)) % (1 << 32)
+                assert np.all(dt < 10_000_000)  # < 0.1 s at 100 MHz
+            elif trace:
                 recs = sess.read_trace()
                 cnt = sess.read_counters()
                 sess.check_trace(recs, s, cnt)
@@ -84,6 +92,12 @@ def test_tiny_merge_variants(tiny, merge_tasks):
     # 1: one merge task per (sequence, kv head); 2: the last chunk merges
     w, prep = tiny
     reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=3, merge_tasks=merge_tasks)
+    assert_reports(reports)
+
+
+def test_tiny_timing_trace(tiny):
+    w, prep = tiny
+    reports, _ = run_steps(w, prep, mk.MK_PERSISTENT, steps=2, trace=2)
     assert_reports(reports)
 
 

@@ -191,6 +191,19 @@ def test_checker_rejects_tampered_traces():
         mk.mk_destroy_graph(g)
 
 
+def test_timing_trace_is_not_checkable():
+    g = build(TINY.shape, num_workers=8, trace=2)
+    try:
+        recs, cnt = mk.mk_simulate(g, steps=1)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_check_trace(g, recs, 0, cnt)
+        assert e.value.status == mk.MK_ERR_ARG
+    finally:
+        mk.mk_destroy_graph(g)
+    with pytest.raises(mk.MkError):
+        build(TINY.shape, trace=3)
+
+
 def test_protocol_under_thread_sanitizer(tmp_path):
     from decode_megakernel_persistent_amd import build as b
     exe = b.build_tsan()
