@@ -186,15 +186,21 @@ struct Ctx {
   const int* pos;  // this step's positions, copied to LDS at kernel entry
 };
 
-DEV u32 event_total(const StepArgs& a, int ev, int lane) {
+// One poll of an event: lane i < kSubCounters loads sub-counter i
+// (agent scope); poll_total sums them (uniform result).
+DEV u32 poll_issue(const StepArgs& a, int ev, int lane) {
   u32 v = 0;
   if (lane < kSubCounters)
     v = __hip_atomic_load(gp(a.counters + ((size_t)ev * kSubCounters + lane) * kCounterStride), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+DEV u32 poll_total(u32 v) {
 #pragma unroll
   for (int o = 1; o < kSubCounters; o <<= 1) v += __shfl_xor(v, o);
   return (u32)__builtin_amdgcn_readlane((int)v, 0);
 }
+DEV u32 event_total(const StepArgs& a, int ev, int lane) { return poll_total(poll_issue(a, ev, lane)); }
 
 DEV void report_timeout(const StepArgs& a, int task, int ev, u32 seen, u32 target) {
   u32 z = 0;
@@ -212,6 +218,8 @@ DEV void report_timeout(const StepArgs& a, int task, int ev, u32 seen, u32 targe
 
 // Wavefront 0 only: poll the task's dependency event until it reaches its
 // target (bounded by the watchdog budget), then take the trace start ticket.
+constexpr int kPolls = 2;         // polls in flight
+constexpr int kPollStagger = 4;   // s_sleep units between the first polls
 DEV void poll_dep(Ctx& c) {
   const StepArgs& a = *c.a;
   const int lane = threadIdx.x & 63;
@@ -222,12 +230,28 @@ DEV void poll_dep(Ctx& c) {
     if (ev >= 0) {
       const u32 target = (u32)a.events[ev].need * (a.epoch + 1u);
       seen = event_total(a, ev, lane);
-      if (!c.lpt) {
+      if (!c.lpt && seen < target) {
+        // kPolls polls in flight, staggered, each re-issued as soon as it is
+        // consumed: the event is seen about a round trip / kPolls after it lands
         const u64 t0 = wall_clock64();
-        int polls = 0;
-        while (seen < target) {
-          __builtin_amdgcn_s_sleep(1);
-          if ((++polls & 31) == 0) {
+        u32 p[kPolls];
+#pragma unroll
+        for (int i = 0; i < kPolls; ++i) {
+          p[i] = poll_issue(a, ev, lane);
+          if (i + 1 < kPolls) __builtin_amdgcn_s_sleep(kPollStagger);
+        }
+        for (int polls = 0;; ++polls) {
+          bool hit = false;
+#pragma unroll
+          for (int i = 0; i < kPolls; ++i) {
+            if (!hit) {
+              seen = poll_total(p[i]);
+              if (seen >= target) hit = true;
+              else p[i] = poll_issue(a, ev, lane);
+            }
+          }
+          if (hit) break;
+          if ((polls & 7) == 7) {
             if (__hip_atomic_load(a.status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
                 wall_clock64() - t0 > a.budget) {
               if (lane == 0) report_timeout(a, c.id, ev, seen, target);
@@ -235,7 +259,6 @@ DEV void poll_dep(Ctx& c) {
               break;
             }
           }
-          seen = event_total(a, ev, lane);
         }
       }
     }

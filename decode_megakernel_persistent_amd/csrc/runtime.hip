@@ -301,11 +301,15 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   }
   Graph& G = *g->G;
   if (G.trace_bytes > 0 && !d_trace) {
-    set_error("mk_load_weights: trace buffer required (graph built with trace=1)");
+    set_error("mk_load_weights: trace buffer required (graph built with trace on)");
     return MK_ERR_ARG;
   }
   if (G.gemv == MK_GEMV_MFMA) {
     set_error("mk_load_weights: MFMA tile layout not available in this build");
+    return MK_ERR_SHAPE;
+  }
+  if (G.shape.n_experts > 0) {
+    set_error("mk_load_weights: routed-expert task bodies are not available in this build");
     return MK_ERR_SHAPE;
   }
   hipStream_t stream = (hipStream_t)stream_;
