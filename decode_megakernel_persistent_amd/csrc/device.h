@@ -447,8 +447,7 @@ DEV u64 gemv_residual_prefetch(const Ctx& c, const OpDesc& op, int NB) {
   return ld_raw(op.res + (size_t)b * op.N + row);
 }
 
-template <int NB>
-DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 res0, const float* rn) {
+DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 res0, const float* rn, int NB) {
   const StepArgs& a = *c.a;
   const int nr = c.t.a2, r0 = c.t.a1, N = op.N;
   for (int j = threadIdx.x; j < NB * nr; j += NT) {
@@ -589,7 +588,7 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
     }
   }
   __syncthreads();
-  gemv_epilogue<NB>(c, op, rsl, NR, res0, rn);
+  gemv_epilogue(c, op, rsl, NR, res0, rn, NB);
 }
 
 // Ring depth (loads per lane).  Deeper rings, also for the O projection that
@@ -610,6 +609,225 @@ template <int NB>
 DEV void gemv_valu_any(Ctx& c, const OpDesc& op) {
   if (op.kind == OP_OPROJ) gemv_valu_s<NB, kRingDeep>(c, op);
   else gemv_valu_s<NB, kRingShallow>(c, op);
+}
+
+// ---------------------------------------------------------------- GEMV (MFMA, batch 5..16)
+// A skinny GEMM on the matrix cores: D[16 rows][16 sequences] += W[16][32] x
+// X[32][16] per v_mfma_f32_16x16x32_bf16, sequences past the batch padded
+// with zeros.  Still bound by the weight stream (16 flop per weight byte at
+// batch 16); the VALU dot products would be LDS-bound here.
+//   weights: 1 KB fragments, fragment (group g of 16 rows, k-block kb of 32
+//     columns) at ((g * K/32 + kb) * 64 + lane) * 16 bytes, lane l holding
+//     row l%16, columns 8*(l/16) .. +8 (laid out at load time);
+//   inputs: staged per chunk of KC columns as bf16 fragments in LDS, fragment
+//     kb at kb * 1 KB, lane l holding sequence l%16, columns 8*(l/16) .. +8;
+//     each value x is split as hi = bf16(x), lo = bf16(x - hi) and both
+//     parts are multiplied (two MFMAs per weight fragment), so the input
+//     keeps about 16 significant bits instead of bf16's 8 (a plain bf16 input
+//     cost ~2% logits error over 36 layers at batch 16).
+// Work items are (row group, K part) pairs: tiles with fewer than eight row
+// groups split K across wavefronts (parts interleaved by k-block) and sum the
+// parts through LDS.  Each wavefront streams its items' fragments through a
+// ring of kMfmaDepth loads; every (chunk, item) segment is padded to whole
+// ring turns so that ring slots stay compile-time indices.
+constexpr int kMfmaKC = 1536;     // input columns staged per chunk (2 x 48 KB of bf16 fragments)
+constexpr int kMfmaDepth = 8;     // weight fragments in flight per wavefront
+constexpr int kMfmaMaxItems = 4;  // items per wavefront (row groups per tile <= 32)
+constexpr int kMfmaVariant = 16;  // kernel template value of the MFMA variant
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+DEV u32 pack_bf16x2(float lo, float hi) { return (u32)f2bf(lo) | ((u32)f2bf(hi) << 16); }
+
+// Stage input columns [c0, c0 + 32*KBc) of every sequence as bf16 fragments
+// (x * g for normalising ops); ss accumulates this thread's sum of squares
+// of its sequence (tid % 16).  Slot s = tid + NT*i covers fragment kb = s/64,
+// lane (s % 64) = sequence s%16, column block (s/16)%4: one 16-byte store.
+DEV void mfma_stage(Ctx& c, const OpDesc& op, int tid, int c0, int KBc, char* xf, char* xl, float& ss) {
+  const StepArgs& a = *c.a;
+  const int B = a.geom->B, K = op.K;
+  const int b = tid & 15;
+  const int nslot = KBc * 64;
+  constexpr int BATCH = 2;  // slots (8 words each) in flight per thread
+  for (int i0 = 0; i0 < (kMfmaKC / 32) * 64 / NT; i0 += BATCH) {
+    if (i0 * NT >= nslot) break;
+    u64 w[BATCH][8];
+    bool ok[BATCH];
+    int kcol[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int s = tid + NT * (i0 + i);
+      const int kb = s >> 6, m = (s >> 4) & 3;
+      kcol[i] = c0 + kb * 32 + m * 8;
+      ok[i] = s < nslot && b < B;
+      const u64* src = op.in + (size_t)(b < B ? b : 0) * K + (ok[i] ? kcol[i] : 0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[i][e] = ld_raw(src + e);
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int s = tid + NT * (i0 + i);
+      if (s < nslot) {
+        u32x4 o = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
+        if (ok[i]) {
+          const u64* src = op.in + (size_t)b * K + kcol[i];
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] = fix_t(w[i][e], src + e, a);
+            ss += v[e] * v[e];
+          }
+          if (op.norm_in) {
+            const f32x4 g0 = *(const f32x4*)(op.g + kcol[i]);
+            const f32x4 g1 = *(const f32x4*)(op.g + kcol[i] + 4);
+            v[0] *= g0.x; v[1] *= g0.y; v[2] *= g0.z; v[3] *= g0.w;
+            v[4] *= g1.x; v[5] *= g1.y; v[6] *= g1.z; v[7] *= g1.w;
+          }
+          float lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          o.z = pack_bf16x2(v[4], v[5]);
+          o.w = pack_bf16x2(v[6], v[7]);
+          ol.x = pack_bf16x2(lo[0], lo[1]);
+          ol.y = pack_bf16x2(lo[2], lo[3]);
+          ol.z = pack_bf16x2(lo[4], lo[5]);
+          ol.w = pack_bf16x2(lo[6], lo[7]);
+        }
+        *(u32x4*)(xf + (size_t)s * 16) = o;
+        *(u32x4*)(xl + (size_t)s * 16) = ol;
+      }
+    }
+  }
+}
+
+DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Task& t = c.t;
+  const int B = a.geom->B, K = op.K, KB = K >> 5;
+  const bool gu = op.kind == OP_GATEUP;
+  const int NR = gu ? 2 * t.a2 : t.a2;
+  const int ngroups = NR >> 4;
+  const int kparts = ngroups >= NWAVE ? 1 : NWAVE / ngroups;
+  const int nitems = ngroups * kparts;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  const int nit = nitems > wave ? (nitems - wave + NWAVE - 1) / NWAVE : 0;
+  const int KC = min(kMfmaKC, K), KBc = KC >> 5, nchunks = (K + KC - 1) / KC;
+  constexpr int DEPTH = kMfmaDepth;
+  const int NJ = (KBc + kparts - 1) / kparts;
+  const int NJp = (NJ + DEPTH - 1) / DEPTH * DEPTH;
+  const uint16_t* Wt = op.w + (size_t)(u32)t.a3;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, (int)((u32)NR * (u32)K * 2u), 0x00020000);
+
+  // fill cursor: chunk fc, item slot fit (its group fg and part fqp), step fj
+  int fc = 0, fit = 0, fj = 0;
+  int fg = wave % max(ngroups, 1), fqp = wave / max(ngroups, 1);
+  auto fill = [&]() -> u32 {
+    u32 off = OOB;
+    if (fc < nchunks && fit < nit) {
+      const int kbl = fqp + fj * kparts, kb = fc * KBc + kbl;
+      if (fj < NJ && kbl < KBc && kb < KB) off = (u32)(((fg * KB + kb) << 6) + lane) << 4;
+    }
+    if (++fj == NJp) {
+      fj = 0;
+      if (++fit >= nit) {
+        fit = 0;
+        ++fc;
+      }
+      const int item = wave + NWAVE * fit;
+      fg = item % max(ngroups, 1);
+      fqp = item / max(ngroups, 1);
+    }
+    return off;
+  };
+  u32x4 buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
+
+  wait_dep(c);
+  char* xf = c.lds;                                  // [KBc][64 lanes][16 B], hi parts
+  char* xl = xf + kMfmaKC / 32 * 1024;               // lo parts
+  float* rsl = (float*)(xl + kMfmaKC / 32 * 1024);   // [B][NR]
+  float* part = rsl + kRowResultFloats;              // [item][16 seq][16 rows]
+  float* red = part + NWAVE * 256;                   // [16 seq][NWAVE]
+  float* rn = red + 16 * NWAVE;                      // [16]
+  const u64 res0 = gemv_residual_prefetch(c, op, B);
+  float ss = 0.f;
+  mfma_stage(c, op, tid, 0, min(KBc, KB), xf, xl, ss);
+  __syncthreads();
+
+  f32x4 acc[kMfmaMaxItems];
+#pragma unroll
+  for (int i = 0; i < kMfmaMaxItems; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const int kbc = min(KBc, KB - cc * KBc);  // k-blocks in this chunk
+    if (cc > 0) {
+      __syncthreads();
+      mfma_stage(c, op, tid, cc * KC, kbc, xf, xl, ss);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int it = 0; it < kMfmaMaxItems; ++it) {
+      if (it < nit) {
+        const int q = (wave + NWAVE * it) / ngroups;
+        for (int j0 = 0; j0 < NJp; j0 += DEPTH) {
+#pragma unroll
+          for (int d = 0; d < DEPTH; ++d) {
+            const int j = j0 + d, kbl = q + j * kparts;
+            if (j < NJ && kbl < kbc) {
+              const u32x4 xv = *(const u32x4*)(xf + (size_t)kbl * 1024 + lane * 16);
+              const u32x4 xw = *(const u32x4*)(xl + (size_t)kbl * 1024 + lane * 16);
+              const bf16x8 wv = __builtin_bit_cast(bf16x8, buf[d]);
+              acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, __builtin_bit_cast(bf16x8, xv), acc[it], 0, 0, 0);
+              acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, __builtin_bit_cast(bf16x8, xw), acc[it], 0, 0, 0);
+            }
+            buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
+          }
+        }
+      }
+    }
+  }
+  // D layout: lane l holds rows 4*(l/16) + r of sequence l%16
+  const int n = lane & 15, r4 = (lane >> 4) * 4;
+  if (kparts == 1) {
+#pragma unroll
+    for (int it = 0; it < kMfmaMaxItems; ++it) {
+      if (it < nit && n < B) {
+        const int g = (wave + NWAVE * it) % ngroups;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rsl[n * NR + g * 16 + r4 + r] = acc[it][r];
+      }
+    }
+  } else if (nit > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave * 256 + n * 16 + r4 + r] = acc[0][r];
+  }
+  // sum of squares per sequence: lanes l, l^16, l^32, l^48 share a sequence
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  if (lane < 16) red[lane * NWAVE + wave] = ss;
+  __syncthreads();
+  if (kparts > 1) {
+    for (int j = tid; j < B * NR; j += NT) {
+      const int nn = j / NR, row = j - nn * NR, g = row >> 4, i = row & 15;
+      float sum = 0.f;
+      for (int q = 0; q < kparts; ++q) sum += part[(q * ngroups + g) * 256 + nn * 16 + i];
+      rsl[nn * NR + row] = sum;
+    }
+  }
+  if (tid < B) {
+    float r = 1.0f;
+    if (op.norm_in) {
+      float tt = 0.f;
+#pragma unroll
+      for (int w8 = 0; w8 < NWAVE; ++w8) tt += red[tid * NWAVE + w8];
+      r = rsqrtf(tt / (float)K + a_eps(c));
+    }
+    rn[tid] = r;
+  }
+  __syncthreads();
+  gemv_epilogue(c, op, rsl, NR, res0, rn, B);
 }
 
 // ---------------------------------------------------------------- group reductions

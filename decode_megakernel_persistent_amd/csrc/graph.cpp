@@ -108,7 +108,13 @@ void build_decoder_ops(Graph& g) {
   const int32_t PW = G * (D + 2);          // partial words of one (b, g, chunk)
   // Tiles per GEMV op: one per worker, more if the per-row results of a tile
   // (batch x rows x mult floats) would not fit the LDS result area.
-  auto max_rows = [&](int32_t mult) { return std::max(1, kRowResultFloats / (mult * B)); };
+  // rows per tile: the per-row results of a tile (batch x rows x mult floats)
+  // must fit the LDS result area; MFMA tiles hold at most 32 row groups
+  auto max_rows = [&](int32_t mult) {
+    int32_t r = std::max(1, kRowResultFloats / (mult * B));
+    if (g.gemv == MK_GEMV_MFMA) r = std::min(r, 512 / mult);
+    return r;
+  };
   auto ntiles = [&](int32_t rows, int32_t mult) {
     const int32_t mr = max_rows(mult) / gr * gr;
     return std::max(W, (rows + mr - 1) / std::max(mr, 1));
@@ -961,7 +967,7 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   g->W = workers;
   g->fuse = fuse;
   int32_t gm = o.gemv;
-  if (gm == MK_GEMV_AUTO) gm = batch >= 8 ? MK_GEMV_MFMA : MK_GEMV_VALU;
+  if (gm == MK_GEMV_AUTO) gm = batch > 4 ? MK_GEMV_MFMA : MK_GEMV_VALU;
   if (gm != MK_GEMV_VALU && gm != MK_GEMV_MFMA) {
     delete g;
     return bad("unknown gemv mode");
@@ -1018,6 +1024,7 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   ge.V = s.vocab;
   ge.L = s.n_layers;
   ge.C = g->C;
+  ge.mfma = g->gemv == MK_GEMV_MFMA ? 1 : 0;
   ge.cap = cap;
   ge.E = s.n_experts;
   ge.topk = s.top_k;

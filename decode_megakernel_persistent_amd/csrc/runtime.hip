@@ -1,7 +1,7 @@
 // runtime.hip - kernels and the host side of the C ABI (include/mk.h).
 //
 // Persistent mode: one cooperative launch of mk_worker with one 512-thread
-// workgroup per compute unit (the 128 KB LDS request leaves room for only one
+// workgroup per compute unit (the 140 KB LDS request leaves room for only one
 // per CU) plus a one-wavefront mk_dispatch kernel on an internal second
 // stream, as the MPK pages split worker and scheduler kernels onto two
 // streams (page "Mirage Persistent Kernel (MPK)", section 5.1).  Each worker
@@ -20,6 +20,7 @@
 #include <cstring>
 #include <map>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "device.h"
@@ -47,7 +48,8 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
     case OP_DOWN:
     case OP_LMHEAD:
     case OP_ROUTER:
-      gemv_valu_any<NB>(c, op);
+      if constexpr (NB == kMfmaVariant) gemv_mfma(c, op);
+      else gemv_valu_any<NB>(c, op);
       break;
     case OP_ATTN:
       body_attn(c, op);
@@ -161,23 +163,29 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
   }
 }
 
+// Kernel variants: 1..4 = VALU GEMV for that batch, kMfmaVariant = MFMA GEMV
+// (any batch up to 16).  Separate instantiations keep each one's register
+// allocation to the GEMV it actually runs.
 typedef void (*kernel_fn)(StepArgs);
-static const void* worker_fn(int nb) {
-  switch (nb) {
+static const void* worker_fn(int v) {
+  switch (v) {
     case 1: return (const void*)mk_worker<1>;
     case 2: return (const void*)mk_worker<2>;
     case 3: return (const void*)mk_worker<3>;
-    default: return (const void*)mk_worker<4>;
+    case 4: return (const void*)mk_worker<4>;
+    default: return (const void*)mk_worker<kMfmaVariant>;
   }
 }
-static const void* lpt_fn(int nb) {
-  switch (nb) {
+static const void* lpt_fn(int v) {
+  switch (v) {
     case 1: return (const void*)mk_lpt<1>;
     case 2: return (const void*)mk_lpt<2>;
     case 3: return (const void*)mk_lpt<3>;
-    default: return (const void*)mk_lpt<4>;
+    case 4: return (const void*)mk_lpt<4>;
+    default: return (const void*)mk_lpt<kMfmaVariant>;
   }
 }
+static int kernel_variant(const Graph& G) { return G.gemv == MK_GEMV_MFMA ? kMfmaVariant : G.B; }
 
 }  // namespace mk
 
@@ -284,6 +292,46 @@ mk_status mk_workspace_size(const mk_graph* g, size_t* arena_bytes, size_t* scra
   return MK_OK;
 }
 
+// MFMA weight fragments: rows [row0, row0 + nrows) of a [rows, K] bf16 tensor
+// become 1 KB fragments of 16 rows x 32 columns, fragment (g, kb) at
+// ((g * K/32 + kb) * 64 + lane) * 16 bytes, lane l holding row 16g + l%16,
+// columns 32kb + 8(l/16) .. +8 (the A-operand layout of
+// v_mfma_f32_16x16x32_bf16).  Done on the host in batches of 1024 rows.
+static bool swizzle16(const CopyJob& cj, const mk_tensor* t, const char* src, char* arena, hipStream_t stream) {
+  const int64_t K = t->cols, KB = K / 32, ngroups = cj.nrows / 16;
+  if (cj.nrows % 16 || K % 32) {
+    set_error("mk_load_weights: MFMA fragments need rows in multiples of 16 and K in multiples of 32");
+    return false;
+  }
+  const int64_t GB = 64;  // groups per batch
+  std::vector<uint16_t> in((size_t)(GB * 16 * K)), out(in.size());
+  const unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  for (int64_t g0 = 0; g0 < ngroups; g0 += GB) {
+    const int64_t ng = std::min(GB, ngroups - g0);
+    const size_t bytes = (size_t)(ng * 16 * K * 2);
+    const char* s = src + (size_t)(g0 * 16 * K * 2);
+    if (t->on_device) {
+      if (hipMemcpy(in.data(), s, bytes, hipMemcpyDeviceToHost) != hipSuccess) return false;
+    } else {
+      std::memcpy(in.data(), s, bytes);
+    }
+    std::vector<std::thread> pool;
+    for (unsigned w = 0; w < nth; ++w)
+      pool.emplace_back([&, w] {
+        for (int64_t g = w; g < ng; g += nth)
+          for (int64_t kb = 0; kb < KB; ++kb)
+            for (int l = 0; l < 64; ++l)
+              std::memcpy(&out[(size_t)(((g * KB + kb) * 64 + l) * 8)],
+                          &in[(size_t)((g * 16 + (l & 15)) * K + kb * 32 + (l >> 4) * 8)], 16);
+      });
+    for (auto& th : pool) th.join();
+    if (hipMemcpy(arena + cj.dst + (size_t)(g0 * 16 * K * 2), out.data(), bytes, hipMemcpyHostToDevice) != hipSuccess)
+      return false;
+  }
+  (void)stream;
+  return true;
+}
+
 // GEMV weight loads per lane issued before the dependency wait.  A load
 // issue blocks once the compute unit's outstanding-miss capacity is full, so
 // a deep pre-wait burst delays the wait and the input staging behind data
@@ -303,10 +351,6 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   if (G.trace_bytes > 0 && !d_trace) {
     set_error("mk_load_weights: trace buffer required (graph built with trace on)");
     return MK_ERR_ARG;
-  }
-  if (G.gemv == MK_GEMV_MFMA) {
-    set_error("mk_load_weights: MFMA tile layout not available in this build");
-    return MK_ERR_SHAPE;
   }
   if (G.shape.n_experts > 0) {
     set_error("mk_load_weights: routed-expert task bodies are not available in this build");
@@ -380,6 +424,8 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
         std::memcpy(&hf[i], &u, 4);
       }
       HIPCHK(hipMemcpy(arena + cj.dst, hf.data(), hf.size() * 4, hipMemcpyHostToDevice));
+    } else if (cj.kind == CopyJob::SWZ16) {
+      if (!swizzle16(cj, t, src, arena, stream)) return MK_ERR_HIP;
     } else {
       set_error("mk_load_weights: unsupported copy kind");
       return MK_ERR_SHAPE;
@@ -437,15 +483,15 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   HIPCHK(hipDeviceGetAttribute(&wcr, hipDeviceAttributeWallClockRate, dev));
   const int64_t us = G.opts.spin_timeout_us > 0 ? G.opts.spin_timeout_us : 2000000;
   g->budget_ticks = (uint64_t)us * (uint64_t)(wcr > 0 ? wcr : 100000) / 1000ull;
-  for (int nb = 1; nb <= 4; ++nb) {
-    (void)hipFuncSetAttribute(worker_fn(nb), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    (void)hipFuncSetAttribute(lpt_fn(nb), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  for (int v : {1, 2, 3, 4, (int)kMfmaVariant}) {
+    (void)hipFuncSetAttribute(worker_fn(v), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    (void)hipFuncSetAttribute(lpt_fn(v), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   }
   (void)hipGetLastError();
   // co-residency: two worker wavefronts per SIMD plus the dispatch wavefront
   {
     hipFuncAttributes fw, fd;
-    HIPCHK(hipFuncGetAttributes(&fw, worker_fn(G.B)));
+    HIPCHK(hipFuncGetAttributes(&fw, worker_fn(kernel_variant(G))));
     HIPCHK(hipFuncGetAttributes(&fd, (const void*)mk_dispatch));
     auto gran = [](int v) { return (v + 7) / 8 * 8; };
     if (2 * gran(fw.numRegs) + gran(fd.numRegs) > 512 || fw.localSizeBytes > 0) {
@@ -519,7 +565,7 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
   a.magic = G.geom.magic;
   a.trace_on = G.opts.trace;
   a.n_workers = G.W;
-  const int nb = G.B;
+  const int nb = kernel_variant(G);
   if (a.trace_on == 1) HIPCHK(hipMemsetAsync(a.status + ST_TICKET, 0, 2 * sizeof(u32), stream));
   if (g->mode == MK_PERSISTENT) {
     hipStream_t side = (hipStream_t)g->side_stream;

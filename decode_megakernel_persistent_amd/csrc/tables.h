@@ -82,7 +82,7 @@ struct Geom {
   float eps;
   float attn_scale;     // 1/sqrt(D)
   uint32_t magic;       // configuration hash checked by every worker at entry
-  int32_t pad;
+  int32_t mfma;         // 1: GEMV tiles use the MFMA path (swizzled weight fragments)
   const double* inv_freq;  // RoPE inverse frequencies [D/2]
 };
 
@@ -111,7 +111,7 @@ enum StatusWord : int32_t {
 };
 
 // LDS budget of one worker (bytes) and the areas the task bodies use.
-constexpr int kLdsBytes = 128 * 1024;
+constexpr int kLdsBytes = 140 * 1024;  // dynamic LDS per worker (gfx950: 160 KB per CU)
 constexpr int kStageFloats = 24576;      // GEMV input staging (96 KB)
 constexpr int kRowResultFloats = 8192;   // GEMV per-row results (32 KB)
 constexpr int kScoreFloats = 8192;       // attention scores of one chunk (32 KB)

@@ -74,7 +74,7 @@ typedef struct {
 #define MK_PERSISTENT 0
 #define MK_LAUNCH_PER_TASK 1
 
-#define MK_GEMV_AUTO 0 /* VALU dot products below batch 8, MFMA from batch 8 */
+#define MK_GEMV_AUTO 0 /* VALU dot products up to batch 4, MFMA skinny GEMM above */
 #define MK_GEMV_VALU 1
 #define MK_GEMV_MFMA 2
 

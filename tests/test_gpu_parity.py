@@ -109,6 +109,20 @@ def test_tiny_one_chunk_and_many_chunks(tiny):
         assert_reports(reports)
 
 
+@pytest.mark.parametrize("batch,gemv", [(1, mk.MK_GEMV_MFMA), (3, mk.MK_GEMV_AUTO), (8, mk.MK_GEMV_AUTO),
+                                        (16, mk.MK_GEMV_AUTO)])
+def test_tiny_batches(batch, gemv):
+    # batch 3: VALU dot products; batch 8 / 16 (and batch 1 when forced): the
+    # MFMA skinny-GEMM tiles, with zero-padded sequences past the batch
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["tiny"], name=f"tiny-b{batch}", batch=batch)
+    prep = harness.prepare(w)
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=3, gemv=gemv)
+    assert_reports(reports)
+    reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=1, trace=False, gemv=gemv)
+    assert_reports(reports)
+
+
 @pytest.fixture(scope="module", params=["qwen3-0.6b", "qwen3-1.7b", "qwen3-8b"])
 def dense(request):
     w = synth.WORKLOADS[request.param]
@@ -126,3 +140,20 @@ def test_dense_parity_launch_per_task(dense):
     w, prep = dense
     reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=2, trace=False)
     assert_reports(reports)
+
+
+@pytest.fixture(scope="module")
+def b16():
+    w = synth.WORKLOADS["qwen3-8b-b16"]
+    return w, harness.prepare(w)
+
+
+def test_8b_batch16_ragged_parity(b16):
+    # 16 sequences with independent positions U{1..2048}; MFMA GEMV tiles
+    w, prep = b16
+    assert len(set(prep.positions.tolist())) > 8
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=2)
+    assert_reports(reports)
+    reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=1, trace=False)
+    assert_reports(reports)
+
