@@ -1160,6 +1160,432 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
   }
 }
 
+// ---------------------------------------------------------------- routed experts
+// Routing table of one layer (tagged words; ids and counts as exact floats):
+//   [b*K*2 + 2j], [+1]      expert and weight of sequence b's j-th choice
+//   TB = B*K*2: expert e at TB + e*(B+1): token count, then the count slots
+//                (slot = b*K + j, in increasing b)
+//   TA = TB + E*(B+1): number of active experts, then the active experts in
+//                increasing id order
+// The router (a GEMV over the normalised residual) leaves logits [B][E]; the
+// dispatch wavefront turns them into this table, the pages' just-in-time
+// expert scheduling ([Review], MoE notes).  Expert gate-up and down tasks
+// are static per-worker slots that split the active experts' work between
+// them; inactive experts cost nothing, and the task counts stay static.
+DEV int route_tb(const Geom& G) { return G.B * G.topk * 2; }
+DEV int route_ta(const Geom& G) { return route_tb(G) + G.E * (G.B + 1); }
+
+// One wavefront (lanes 0..63): softmax over E <= 256 experts, top-K (ties to
+// the lower id), renormalised weights, expert token lists, active list.
+DEV void route_wave(const StepArgs& a, const OpDesc& op, int lane) {
+  const Geom& G = *a.geom;
+  const int B = G.B, E = G.E, K = G.topk;
+  __shared__ int s_e[16 * 8];
+  u64* route = op.out;
+  for (int b = 0; b < B; ++b) {
+    const u64* lg = op.in + (size_t)b * E;
+    u64 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = ld_raw(lg + min(lane + 64 * i, E - 1));
+    float p[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      p[i] = e < E ? fix_t(w[i], lg + e, a) : -INFINITY;
+      m = fmaxf(m, p[i]);
+    }
+    m = wave_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = lane + 64 * i < E ? expf(p[i] - m) : 0.f;
+      sum += p[i];
+    }
+    sum = wave_sum(sum);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = lane + 64 * i < E ? p[i] / sum : -1.f;
+    float tot = 0.f, wj = 0.f;
+    int ej = 0;
+    for (int j = 0; j < K; ++j) {
+      // this lane's best remaining (lower id wins ties), then the wavefront's
+      float bv = -1.f;
+      int be = 1 << 30;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (p[i] > bv) {
+          bv = p[i];
+          be = lane + 64 * i;
+        }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oe = __shfl_xor(be, o);
+        if (ov > bv || (ov == bv && oe < be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i == be) p[i] = -1.f;
+      if (lane == j) {
+        ej = be;
+        wj = bv;
+      }
+      tot += bv;
+    }
+    if (lane < K) {
+      s_e[b * K + lane] = ej;
+      st_t(route + (size_t)(b * K + lane) * 2, (float)ej, a.tag);
+      st_t(route + (size_t)(b * K + lane) * 2 + 1, wj / tot, a.tag);
+    }
+  }
+  // one wavefront: its LDS writes above complete before the reads below
+  // (no hardware barrier: in a launch-per-task workgroup only wave 0 is here)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  u64* table = route + route_tb(G);
+  u64* act = route + route_ta(G);
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    int cnt = 0;
+    if (e < E) {
+      for (int sl = 0; sl < B * K; ++sl)
+        if (s_e[sl] == e) {
+          st_t(table + (size_t)e * (B + 1) + 1 + cnt, (float)sl, a.tag);
+          ++cnt;
+        }
+      st_t(table + (size_t)e * (B + 1), (float)cnt, a.tag);
+    }
+    const u64 mask = __ballot(cnt > 0);
+    const int before = __builtin_popcountll(mask & ((1ull << lane) - 1ull));
+    if (cnt > 0) st_t(act + 1 + base + before, (float)e, a.tag);
+    base += __builtin_popcountll(mask);
+  }
+  if (lane == 0) st_t(act, (float)base, a.tag);
+}
+
+// All threads: xs[b][k] = rmsnorm(in[b]) * g for every sequence (fp32 in LDS).
+DEV void moe_stage_norm(Ctx& c, const OpDesc& op, int tid, float* xs, float* red) {
+  const StepArgs& a = *c.a;
+  const int B = a.geom->B, H = op.K;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int b = 0; b < B; ++b) {
+    const u64* in = op.in + (size_t)b * H;
+    float ss = 0.f;
+    for (int k0 = 0; k0 < H; k0 += NT * 8) {
+      u64 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = ld_raw(in + min(k0 + tid + i * NT, H - 1));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = k0 + tid + i * NT;
+        if (k < H) {
+          const float v = fix_t(w[i], in + k, a);
+          xs[b * H + k] = v * ldg(op.g + k);
+          ss += v * v;
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[b * NWAVE + wave] = ss;
+  }
+  __syncthreads();
+  for (int b = 0; b < B; ++b) {
+    float t = 0.f;
+#pragma unroll
+    for (int w8 = 0; w8 < NWAVE; ++w8) t += red[b * NWAVE + w8];
+    const float r = rsqrtf(t / (float)H + a.geom->eps);
+    for (int k = tid; k < H; k += NT) xs[b * H + k] *= r;
+  }
+  __syncthreads();
+}
+
+// Items [i0, i1) of this slot task: item = (active expert act[item / U],
+// unit item % U).  Loads the active list into LDS (ids as ints).
+DEV int moe_load_active(Ctx& c, const u64* act, int* s_act, int tid) {
+  const StepArgs& a = *c.a;
+  const int n = (int)ld_t(act, a);
+  for (int i = tid; i < n; i += NT) s_act[i] = (int)ld_t(act + 1 + i, a);
+  __syncthreads();
+  return n;
+}
+// Token list of expert e into LDS: s_tok[t] = slot (b*K + j); returns the count.
+DEV int moe_load_tokens(Ctx& c, const u64* table, int e, int* s_tok, int tid) {
+  const StepArgs& a = *c.a;
+  const int B = a.geom->B;
+  const u64* te = table + (size_t)e * (B + 1);
+  __syncthreads();
+  if (tid == 0) s_tok[16] = (int)ld_t(te, a);
+  __syncthreads();
+  const int n = s_tok[16];
+  if (tid < n) s_tok[tid] = (int)ld_t(te + 1 + tid, a);
+  __syncthreads();
+  return n;
+}
+
+// Expert gate-up slot: for each item (expert e, 16-row unit u) and each token
+// of e: act[slot][16u + r] = silu(gate_r . h) * (up_r . h).  Weights of one
+// unit: 16 gate rows then 16 up rows, rows of H contiguous bf16.  Wavefront w
+// computes outputs r = w and w + 8 (gate and up rows in the same wavefront);
+// an 8-load ring streams (item, output, gate/up, chunk) in order, 16 loads per
+// item per lane.
+DEV void body_moe_gu(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int B = G.B, K = G.topk, Ie = G.Ie, H = op.K;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  const int U = Ie / 16;
+  float* xs = (float*)c.lds;                                   // [B][H]
+  int* s_act = (int*)(c.lds + (size_t)kStageFloats * 4);       // [E]
+  int* s_tok = s_act + 256;                                    // [16 + 1]
+  float* red = (float*)(s_tok + 32);
+  const u64* route = op.aux;
+  wait_dep(c);
+  const int n_act = moe_load_active(c, route + route_ta(G), s_act, tid);
+  const int total = n_act * U, ns = op.ntasks, s = c.t.a0;
+  const int i0 = (int)((long)s * total / ns), i1 = (int)((long)(s + 1) * total / ns);
+  const int nchunk = (H / 8 + 63) / 64;  // 16-byte chunks per lane per row (H = 2048: 4)
+  if (i1 <= i0) return;  // uniform across the workgroup
+  moe_stage_norm(c, op, tid, xs, red);
+  // weights of every expert: [E][2*Ie][H]; unit u of e starts at row e*2*Ie + 32u
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)op.w, (short)0, (int)((u32)G.E * 2u * (u32)Ie * (u32)H * 2u), 0x00020000);
+  constexpr int DEPTH = 8;
+  const int NL = 4 * nchunk;                  // loads per item per lane (2 outputs x gate/up x chunks)
+  const int NLp = (NL + DEPTH - 1) / DEPTH * DEPTH;
+  int fi = i0, fl = 0;
+  auto fill = [&]() -> u32 {
+    u32 off = OOB;
+    if (fi < i1 && fl < NL) {
+      const int e = s_act[fi / U], u = fi - (fi / U) * U;
+      const int o = fl / (2 * nchunk), gu = (fl / nchunk) & 1, q = fl % nchunk;
+      const int row = e * 2 * Ie + u * 32 + gu * 16 + wave + 8 * o;
+      const int cc = q * 64 + lane;
+      if (cc * 8 < H) off = (u32)((row * H + cc * 8) * 2);
+    }
+    if (++fl == NLp) {
+      fl = 0;
+      ++fi;
+    }
+    return off;
+  };
+  u32x4 buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
+  int cur_e = -1, ntok = 0;
+  const u64* table = route + route_tb(G);
+  for (int it = i0; it < i1; ++it) {
+    const int e = s_act[it / U], u = it - (it / U) * U;
+    if (e != cur_e) {
+      ntok = moe_load_tokens(c, table, e, s_tok, tid);
+      cur_e = e;
+    }
+    float acc[2][2][8];  // [output][gate/up][token]
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[o][g2][t] = 0.f;
+    for (int l0 = 0; l0 < NLp; l0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int l = l0 + d;
+        if (l < NL) {
+          const int o = l / (2 * nchunk), gu = (l / nchunk) & 1, q = l % nchunk;
+          const int cc = q * 64 + lane;
+          if (cc * 8 < H) {
+            const u32x4 wv = buf[d];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              if (t < ntok) {
+                const int b = s_tok[t] / K;
+                const f32x4 x0 = *(const f32x4*)(xs + b * H + cc * 8);
+                const f32x4 x1 = *(const f32x4*)(xs + b * H + cc * 8 + 4);
+                float sacc = bf_lo(wv.x) * x0.x;
+                sacc = fmaf(bf_hi(wv.x), x0.y, sacc);
+                sacc = fmaf(bf_lo(wv.y), x0.z, sacc);
+                sacc = fmaf(bf_hi(wv.y), x0.w, sacc);
+                sacc = fmaf(bf_lo(wv.z), x1.x, sacc);
+                sacc = fmaf(bf_hi(wv.z), x1.y, sacc);
+                sacc = fmaf(bf_lo(wv.w), x1.z, sacc);
+                sacc = fmaf(bf_hi(wv.w), x1.w, sacc);
+                // o and gu are uniform: select the accumulator without dynamic indexing
+                if (o == 0 && gu == 0) acc[0][0][t] += sacc;
+                else if (o == 0) acc[0][1][t] += sacc;
+                else if (gu == 0) acc[1][0][t] += sacc;
+                else acc[1][1][t] += sacc;
+              }
+            }
+          }
+        }
+        buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
+      }
+    }
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < ntok) {
+          const float gsum = wave_sum(acc[o][0][t]), usum = wave_sum(acc[o][1][t]);
+          if (lane == 0) st_t(op.out + (size_t)s_tok[t] * Ie + u * 16 + wave + 8 * o, silu(gsum) * usum, a.tag);
+        }
+      }
+  }
+}
+
+// Expert down slot: for each item (expert e, 64-row unit u) and token of e:
+// y[slot][64u + row] = W_down[e][64u + row] . act[slot].  Wavefront w takes
+// rows w, w+8, ..., w+56; lanes read 16-byte chunks of the Ie-long rows.
+DEV void body_moe_down(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int Ie = op.K, H = op.N;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  const int U = H / 64;
+  float* xin = (float*)c.lds;                                  // [16 tokens][Ie]
+  int* s_act = (int*)(c.lds + (size_t)kStageFloats * 4);
+  int* s_tok = s_act + 256;
+  const u64* route = op.aux;
+  wait_dep(c);
+  const int n_act = moe_load_active(c, route + route_ta(G), s_act, tid);
+  const int total = n_act * U, ns = op.ntasks, s = c.t.a0;
+  const int i0 = (int)((long)s * total / ns), i1 = (int)((long)(s + 1) * total / ns);
+  if (i1 <= i0) return;
+  const int nchunk = (Ie / 8 + 63) / 64;  // Ie = 768: 2
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)op.w, (short)0, (int)((u32)G.E * (u32)H * (u32)Ie * 2u), 0x00020000);
+  constexpr int DEPTH = 8;
+  const int NL = 8 * nchunk;
+  const int NLp = (NL + DEPTH - 1) / DEPTH * DEPTH;
+  int fi = i0, fl = 0;
+  auto fill = [&]() -> u32 {
+    u32 off = OOB;
+    if (fi < i1 && fl < NL) {
+      const int e = s_act[fi / U], u = fi - (fi / U) * U;
+      const int r = fl / nchunk, q = fl % nchunk;
+      const int row = e * H + u * 64 + wave + 8 * r;
+      const int cc = q * 64 + lane;
+      if (cc * 8 < Ie) off = (u32)((row * Ie + cc * 8) * 2);
+    }
+    if (++fl == NLp) {
+      fl = 0;
+      ++fi;
+    }
+    return off;
+  };
+  u32x4 buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
+  int cur_e = -1, ntok = 0;
+  const u64* table = route + route_tb(G);
+  for (int it = i0; it < i1; ++it) {
+    const int e = s_act[it / U], u = it - (it / U) * U;
+    if (e != cur_e) {
+      ntok = moe_load_tokens(c, table, e, s_tok, tid);
+      // the expert's token inputs, all loads in flight before the tag checks
+      constexpr int PT = 8 * 1024 / NT;  // words per thread for up to 8 tokens of Ie <= 1024
+      u64 wv[PT];
+      const int n = ntok * Ie;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int j = min(tid + i * NT, max(n - 1, 0));
+        const int t = j / Ie, k = j - t * Ie;
+        wv[i] = ld_raw(op.in + (size_t)s_tok[t] * Ie + k);
+      }
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int j = tid + i * NT;
+        if (j < n) {
+          const int t = j / Ie, k = j - t * Ie;
+          xin[t * Ie + k] = fix_t(wv[i], op.in + (size_t)s_tok[t] * Ie + k, a);
+        }
+      }
+      __syncthreads();
+      cur_e = e;
+    }
+    float acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+    for (int l0 = 0; l0 < NLp; l0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int l = l0 + d;
+        if (l < NL) {
+          const int r = l / nchunk, q = l % nchunk;
+          const int cc = q * 64 + lane;
+          if (cc * 8 < Ie) {
+            const u32x4 wv = buf[d];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              if (t < ntok) {
+                const f32x4 x0 = *(const f32x4*)(xin + t * Ie + cc * 8);
+                const f32x4 x1 = *(const f32x4*)(xin + t * Ie + cc * 8 + 4);
+                float sacc = bf_lo(wv.x) * x0.x;
+                sacc = fmaf(bf_hi(wv.x), x0.y, sacc);
+                sacc = fmaf(bf_lo(wv.y), x0.z, sacc);
+                sacc = fmaf(bf_hi(wv.y), x0.w, sacc);
+                sacc = fmaf(bf_lo(wv.z), x1.x, sacc);
+                sacc = fmaf(bf_hi(wv.z), x1.y, sacc);
+                sacc = fmaf(bf_lo(wv.w), x1.z, sacc);
+                sacc = fmaf(bf_hi(wv.w), x1.w, sacc);
+                acc[t] += sacc;
+              }
+            }
+          }
+          if (q == nchunk - 1) {
+            // row r complete: reduce and store per token
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              if (t < ntok) {
+                const float v = wave_sum(acc[t]);
+                if (lane == 0) st_t(op.out + (size_t)s_tok[t] * H + u * 64 + wave + 8 * r, v, a.tag);
+              }
+              acc[t] = 0.f;
+            }
+          }
+        }
+        buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
+      }
+    }
+  }
+}
+
+// x_out[b][h] = x_res[b][h] + sum_j w[b][j] * y[b*K + j][h] for the tile's rows.
+DEV void body_combine(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int B = G.B, K = G.topk, H = op.N;
+  const int r0 = c.t.a1, nr = c.t.a2;
+  wait_dep(c);
+  for (int j = task_tid(); j < B * nr; j += NT) {
+    const int b = j / nr, h = r0 + (j - b * nr);
+    // residual, K weights and K expert outputs: one batch of loads
+    const u64* rp = op.res + (size_t)b * H + h;
+    const u64 wr = ld_raw(rp);
+    u64 ww[8], wy[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int kk = min(k, K - 1);
+      ww[k] = ld_raw(op.aux + (size_t)(b * K + kk) * 2 + 1);
+      wy[k] = ld_raw(op.in + (size_t)(b * K + kk) * H + h);
+    }
+    float v = fix_t(wr, rp, a);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < K) {
+        const float wk = fix_t(ww[k], op.aux + (size_t)(b * K + k) * 2 + 1, a);
+        v = fmaf(wk, fix_t(wy[k], op.in + (size_t)(b * K + k) * H + h, a), v);
+      }
+    }
+    st_t(op.out + (size_t)b * H + h, v, a.tag);
+  }
+}
+
 DEV void body_attn(Ctx& c, const OpDesc& op) {
   const Geom& G = *c.a->geom;
   const bool d128 = G.D == 128;

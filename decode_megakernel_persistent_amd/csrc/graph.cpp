@@ -244,8 +244,9 @@ void build_decoder_ops(Graph& g) {
     } else {
       const int32_t E = s.n_experts, K = s.top_k, Ie = s.expert_intermediate;
       int32_t rlog = bd.buf("rlog" + ls, (int64_t)B * E);
-      // routing table: per sequence K (expert, weight) pairs, then the work list
-      int32_t route = bd.buf("route" + ls, (int64_t)B * K * 2 + 64 + (int64_t)E * (B + 2) + 2LL * E * 64);
+      // routing table: per sequence K (expert, weight) pairs; per expert its
+      // token count and slots; the active-expert list
+      int32_t route = bd.buf("route" + ls, (int64_t)B * K * 2 + (int64_t)E * (B + 1) + E + 1);
       int32_t mact = bd.buf("mact" + ls, (int64_t)B * K * Ie);
       int32_t my = bd.buf("my" + ls, (int64_t)B * K * H);
       {
@@ -847,8 +848,8 @@ void layout(Graph& g) {
           std::string q = p + "experts." + std::to_string(e) + ".";
           for (int32_t r0 = 0; r0 < Ie; r0 += 16) {
             int64_t dst = base + (int64_t)r0 * 2 * H * 2;
-            rows(q + "w_gate", r0, 16, H, dst, wkind);
-            rows(q + "w_up", r0, 16, H, dst + 16LL * H * 2, wkind);
+            rows(q + "w_gate", r0, 16, H, dst, CopyJob::ROWS);
+            rows(q + "w_up", r0, 16, H, dst + 16LL * H * 2, CopyJob::ROWS);
           }
         }
         op.g_off = gain(p + "post_norm", H);
@@ -858,7 +859,8 @@ void layout(Graph& g) {
         const int32_t E = s.n_experts, Ie = s.expert_intermediate;
         op.w_off = take((int64_t)E * H * Ie * 2);
         for (int32_t e = 0; e < E; ++e)
-          rows(p + "experts." + std::to_string(e) + ".w_down", 0, H, Ie, op.w_off + (int64_t)e * H * Ie * 2, wkind);
+          rows(p + "experts." + std::to_string(e) + ".w_down", 0, H, Ie, op.w_off + (int64_t)e * H * Ie * 2,
+               CopyJob::ROWS);
         break;
       }
       case OP_LMHEAD:
@@ -950,6 +952,8 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   if (s.n_experts > 0 && (s.top_k <= 0 || s.top_k > s.n_experts || s.top_k > 8 || s.expert_intermediate % 16 ||
                           s.expert_intermediate <= 0 || s.n_experts > 256))
     return bad("bad expert configuration (top_k <= 8, expert_intermediate multiple of 16, <= 256 experts)");
+  if (s.n_experts > 0 && (batch > 8 || s.expert_intermediate > 1024 || s.hidden % 64))
+    return bad("routed experts support batch <= 8 and expert_intermediate <= 1024");
   if (batch <= 0 || batch > 16) return bad("batch must be in 1..16");
   if (cap <= 0 || cap > (1 << 20)) return bad("max_ctx out of range");
   if (workers <= 0 || workers > 4096) return bad("worker count out of range");

@@ -58,6 +58,20 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
       wait_dep(c);
       body_merge(c, op);
       break;
+    case OP_ROUTE:
+      // normally on the dispatch wavefront; in a launch-per-task workgroup wave 0 routes
+      wait_dep(c);
+      if (threadIdx.x < 64) route_wave(a, op, threadIdx.x);
+      break;
+    case OP_MOE_GU:
+      body_moe_gu(c, op);
+      break;
+    case OP_MOE_DOWN:
+      body_moe_down(c, op);
+      break;
+    case OP_COMBINE:
+      body_combine(c, op);
+      break;
     case OP_EMBED:
       wait_dep(c);
       body_embed(c, op);
@@ -149,6 +163,33 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
       return;
     }
     __builtin_amdgcn_s_sleep(16);
+  }
+  // the dispatcher's own tasks (routing of routed-expert layers), in id order
+  {
+    __shared__ int flags[64];
+    if (threadIdx.x < 64) flags[threadIdx.x] = 0;
+    __syncthreads();
+    for (int k = a.wl_off[W]; k < a.wl_off[W + 1]; ++k) {
+      const int id = a.wl_ids[k];
+      if (threadIdx.x == 0)
+        __hip_atomic_store(a.progress + W, (u32)id + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      Ctx c;
+      c.a = &a;
+      c.t = a.tasks[id];
+      c.id = id;
+      c.agent = W;
+      c.lpt = false;
+      c.lds = nullptr;
+      c.flags = flags;
+      c.pos = nullptr;
+      wait_dep(c);
+      if (flags[0]) return;
+      route_wave(a, a.ops[c.t.op], threadIdx.x);
+      finish(c);
+      __syncthreads();
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.progress + W, 0xFFFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   t0 = wall_clock64();
   for (;;) {
@@ -351,10 +392,6 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   if (G.trace_bytes > 0 && !d_trace) {
     set_error("mk_load_weights: trace buffer required (graph built with trace on)");
     return MK_ERR_ARG;
-  }
-  if (G.shape.n_experts > 0) {
-    set_error("mk_load_weights: routed-expert task bodies are not available in this build");
-    return MK_ERR_SHAPE;
   }
   hipStream_t stream = (hipStream_t)stream_;
   // ---- the tensor set

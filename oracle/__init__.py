@@ -77,6 +77,8 @@ def _load():
     lib.orc_full_forward.restype = ctypes.c_int32
     lib.orc_last_routing.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p, _dp]
     lib.orc_last_routing.restype = ctypes.c_int32
+    lib.orc_last_routing_gap.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.orc_last_routing_gap.restype = ctypes.c_double
     _lib = lib
     return lib
 
@@ -206,6 +208,11 @@ class Oracle:
         if rc:
             raise RuntimeError(_load().orc_last_error().decode())
         return lg
+
+    def last_routing_gap(self, b: int) -> float:
+        """Smallest router-logit gap between a chosen and an unchosen expert of
+        sequence b over the layers of the last decode (inf for dense models)."""
+        return float(_load().orc_last_routing_gap(self._h, b))
 
     def last_routing(self, layer: int, b: int) -> Tuple[np.ndarray, np.ndarray]:
         k = self.shape.top_k

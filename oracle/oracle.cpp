@@ -251,6 +251,7 @@ struct orc_model {
   // routing of the last decode step: [L][B][top_k]
   std::vector<int32_t> route_e;
   std::vector<double> route_w;
+  std::vector<double> route_gap;  // [L][B]: smallest chosen logit minus largest unchosen logit
 };
 
 namespace {
@@ -369,6 +370,16 @@ void ffn_block(orc_model* m, int l, int b, double* x) {
       m->route_e[((size_t)l * m->B + b) * Kt + j] = ex[j];
       m->route_w[((size_t)l * m->B + b) * Kt + j] = wt[j];
     }
+    // how close the top-k choice came to a tie (in logit units): a decision
+    // another precision may take differently when this is tiny
+    double lo_in = INFINITY, hi_out = -INFINITY;
+    std::vector<char> chosen((size_t)E, 0);
+    for (int j = 0; j < Kt; ++j) chosen[ex[j]] = 1;
+    for (int e = 0; e < E; ++e) {
+      if (chosen[e]) lo_in = std::min(lo_in, r[e]);
+      else hi_out = std::max(hi_out, r[e]);
+    }
+    m->route_gap[(size_t)l * m->B + b] = lo_in - hi_out;
   }
   std::vector<double> acc((size_t)H, 0.0);
   for (int j = 0; j < Kt; ++j) {
@@ -415,6 +426,7 @@ orc_model* orc_create(const orc_shape* s, int32_t batch, int32_t cap, int32_t nt
     if (s->n_experts > 0) {
       m->route_e.assign((size_t)s->n_layers * batch * s->top_k, -1);
       m->route_w.assign((size_t)s->n_layers * batch * s->top_k, 0.0);
+      m->route_gap.assign((size_t)s->n_layers * batch, INFINITY);
     }
     return m;
   } catch (const std::exception& e) {
@@ -518,6 +530,15 @@ int32_t orc_full_forward(orc_model* m, const int32_t* tokens, int32_t n, double*
     g_err = e.what();
     return -1;
   }
+}
+
+// Smallest routing gap (chosen minus unchosen router logit) of sequence b
+// over all layers of the last orc_decode; +inf for dense models.
+double orc_last_routing_gap(const orc_model* m, int32_t b) {
+  double g = INFINITY;
+  if (!m || m->s.n_experts == 0) return g;
+  for (int l = 0; l < m->s.n_layers; ++l) g = std::min(g, m->route_gap[(size_t)l * m->B + b]);
+  return g;
 }
 
 // Routing chosen by the last orc_decode for (layer, b): top_k experts and weights.

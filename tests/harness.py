@@ -23,6 +23,14 @@ import synth
 
 REL_L2_TOL = 1e-2
 MARGIN = 0.05
+# Routed experts: the expert choice is an integer decided by floating point.
+# The GPU decides it in fp32 from its own router logits, the oracle in fp64; a
+# (step, sequence) whose oracle routing gap (smallest chosen minus largest
+# unchosen router logit, over all layers) is below this may legitimately
+# route differently, so it is not compared (both results are correct).  The
+# GPU's hidden state is within ~1e-5 relative of the oracle's, so its router
+# logits (|r| ~ 1) are within ~1e-5..1e-4 absolute; 3e-4 leaves a margin.
+ROUTE_GAP_TOL = 3e-4
 
 
 @dataclasses.dataclass
@@ -63,9 +71,13 @@ def prepare(w: synth.Workload, threads: int = 0, weights: Optional[Dict[str, np.
     return Prepared(w, ws, orc, orc.K.copy(), orc.V.copy(), tokens, positions)
 
 
-def compare(lg_gpu: np.ndarray, lg_orc: np.ndarray) -> List[dict]:
+def compare(lg_gpu: np.ndarray, lg_orc: np.ndarray, gaps: Optional[List[float]] = None) -> List[dict]:
     out = []
     for b in range(lg_orc.shape[0]):
+        if gaps is not None and gaps[b] < ROUTE_GAP_TOL:
+            out.append(dict(rel_l2=0.0, margin=0.0, tok_oracle=int(np.argmax(lg_orc[b])),
+                            tok_gpu=int(np.argmax(lg_gpu[b])), ok=True, exempt=True, route_gap=gaps[b]))
+            continue
         ref = lg_orc[b]
         err = float(np.linalg.norm(lg_gpu[b].astype(np.float64) - ref) / np.linalg.norm(ref))
         margin = float(oracle.top2_margin(ref))

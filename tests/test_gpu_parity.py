@@ -38,8 +38,13 @@ def run_steps(w, prep, mode, steps, trace=True, workers=0, gemv=mk.MK_GEMV_AUTO,
             sess.check()
             lg_g = lg_g.cpu().numpy()
             lg_o = orc.decode(tok, pos)
-            rep = harness.compare(lg_g, lg_o)
+            gaps = [orc.last_routing_gap(b) for b in range(w.batch)] if w.shape.n_experts else None
+            rep = harness.compare(lg_g, lg_o, gaps)
             reports.append(rep)
+            if any(r.get("exempt") for r in rep):
+                # a near-tie routing step: resynchronise the GPU cache from the oracle's
+                harness.log(f"[route] step {s}: near-tie routing, gaps {[round(g, 6) for g in gaps]}")
+                sess.set_kv(orc.K, orc.V)
             if trace == 2:
                 # timing trace: record i is task i, stamped by a worker, clocks ordered
                 recs = sess.read_trace()
@@ -62,8 +67,12 @@ def run_steps(w, prep, mode, steps, trace=True, workers=0, gemv=mk.MK_GEMV_AUTO,
 def assert_reports(reports):
     worst = max(r["rel_l2"] for rep in reports for r in rep)
     bad = [(s, b, r) for s, rep in enumerate(reports) for b, r in enumerate(rep) if not r["ok"]]
-    harness.log(f"[parity] steps={len(reports)} worst rel_l2={worst:.3e} failures={len(bad)}")
+    exempt = sum(1 for rep in reports for r in rep if r.get("exempt"))
+    total = sum(len(rep) for rep in reports)
+    harness.log(f"[parity] steps={len(reports)} worst rel_l2={worst:.3e} failures={len(bad)} "
+                f"routing near-ties={exempt}/{total}")
     assert not bad, f"parity failures (step, seq, report): {bad[:5]}"
+    assert exempt * 4 <= total, "too many near-tie routing exemptions for the comparison to mean anything"
 
 
 @pytest.fixture(scope="module")
@@ -153,6 +162,33 @@ def test_8b_batch16_ragged_parity(b16):
     w, prep = b16
     assert len(set(prep.positions.tolist())) > 8
     reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=2)
+    assert_reports(reports)
+    reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=1, trace=False)
+    assert_reports(reports)
+
+
+MOE_SMALL = synth.ModelShape(n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=64, intermediate=0,
+                             vocab=1024, tied_embeddings=False, n_experts=16, top_k=4, expert_intermediate=128)
+
+
+@pytest.mark.parametrize("batch", [2, 8])
+def test_small_moe_parity(batch):
+    # router GEMV, routing on the dispatch wavefront, expert gate-up / down
+    # slots over gathered tokens, combine; batch 2 VALU, batch 8 MFMA router
+    w = synth.Workload(name=f"moe-small-b{batch}", shape=MOE_SMALL, batch=batch, context=96, steps=4, ragged=True)
+    prep = harness.prepare(w)
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=4)
+    assert_reports(reports)
+    reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=2, trace=False)
+    assert_reports(reports)
+
+
+@pytest.mark.slow
+def test_30b_a3b_batch8_parity():
+    # 48 layers, 128 experts, top-8, batch 8 at context 1024 (61 GB of weights)
+    w = synth.WORKLOADS["qwen3-30b-a3b"]
+    prep = harness.prepare(w)
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=3)
     assert_reports(reports)
     reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=1, trace=False)
     assert_reports(reports)
