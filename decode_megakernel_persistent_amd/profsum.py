@@ -69,10 +69,11 @@ def _counter(db: str, counter: str) -> List[Tuple[str, int, float]]:
     return [(n, int(d), float(v)) for n, d, v in rows]
 
 
-def _split(rows, kernel: str, copy_bytes: int):
+def _split(rows, kernel: str, copy_bytes: int, reps: int = 3):
     mine = [v for n, _, v in rows if kernel in n]
-    # the calibration copies: the dispatches that read/write about copy_bytes
-    copies = [v for n, _, v in rows if "copy" in n.lower() and v * 1024 > 0.5 * copy_bytes]
+    # the calibration copies: the last `reps` copy dispatches of the run (the
+    # profile run issues them after the timed steps)
+    copies = [v for n, d, v in sorted(rows, key=lambda r: r[1]) if "copy" in n.lower()][-reps:]
     return mine, copies
 
 
@@ -103,12 +104,20 @@ def traffic(fetch_db: str, write_db: str, kernel: str, copy_mib: int, algorithmi
     if algorithmic > 0:
         lines.append(f"algorithmic_bytes_per_launch = {algorithmic:.0f}")
         lines.append(f"traffic_over_algorithmic = {tot / algorithmic:.4f}")
+    last_f = {d for n, d, v in sorted(f_rows, key=lambda r: r[1]) if "copy" in n.lower()}
+    last_w = {d for n, d, v in sorted(w_rows, key=lambda r: r[1]) if "copy" in n.lower()}
+    cal = set(sorted(last_f)[-3:]) | set(sorted(last_w)[-3:])
+
+    def keep(n, d):
+        return kernel in n or d in cal
     lines += ["", "| dispatch | kernel | FETCH_SIZE KiB |", "|---|---|---|"]
     for n, d, v in f_rows:
-        lines.append(f"| {d} | {_short(n)[:60]} | {v:.0f} |")
+        if keep(n, d):
+            lines.append(f"| {d} | {_short(n)[:60]} | {v:.0f} |")
     lines += ["", "| dispatch | kernel | WRITE_SIZE KiB |", "|---|---|---|"]
     for n, d, v in w_rows:
-        lines.append(f"| {d} | {_short(n)[:60]} | {v:.0f} |")
+        if keep(n, d):
+            lines.append(f"| {d} | {_short(n)[:60]} | {v:.0f} |")
     return "\n".join(lines) + "\n"
 
 
