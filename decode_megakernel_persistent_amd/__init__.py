@@ -67,7 +67,7 @@ class mk_build_opts(ctypes.Structure):
                 ("trace", ctypes.c_int32), ("attn_chunks", ctypes.c_int32), ("gemv", ctypes.c_int32),
                 ("spin_timeout_us", ctypes.c_int32), ("no_fusion", ctypes.c_int32), ("merge_tasks", ctypes.c_int32),
                 ("no_watchdog", ctypes.c_int32), ("prefetch_loads", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 5)]
+                ("late_trigger", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
 
 
 class mk_tensor(ctypes.Structure):
@@ -168,11 +168,12 @@ def make_shape(s) -> mk_model_shape:
 
 def make_opts(mode=MK_PERSISTENT, per_task_launch=0, num_workers=0, trace=0, attn_chunks=0, gemv=MK_GEMV_AUTO,
               spin_timeout_us=0, no_fusion=0, merge_tasks=0, no_watchdog=0,
-              prefetch_loads=0) -> mk_build_opts:
+              prefetch_loads=0, late_trigger=0) -> mk_build_opts:
     o = mk_build_opts()
     o.mode, o.per_task_launch, o.num_workers, o.trace = mode, per_task_launch, num_workers, trace
     o.attn_chunks, o.gemv, o.spin_timeout_us, o.no_fusion = attn_chunks, gemv, spin_timeout_us, no_fusion
     o.merge_tasks, o.no_watchdog, o.prefetch_loads = merge_tasks, no_watchdog, prefetch_loads
+    o.late_trigger = late_trigger
     return o
 
 

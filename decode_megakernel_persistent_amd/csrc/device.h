@@ -286,15 +286,34 @@ DEV void wait_dep(Ctx& c) {
 // records the trace and triggers the task's event.  The trigger does not wait
 // for the stores to be acknowledged: a consumer that reads a word before it
 // lands sees the old tag and re-reads it.
+// Thread 0 only: take the trace end ticket and clock, then add to the task's
+// trigger event.  Called once per task, by finish or earlier by a body whose
+// outputs are about to be stored (flags[5] records that it happened).
+DEV void trigger_event(Ctx& c) {
+  const StepArgs& a = *c.a;
+  if (c.flags[5]) return;
+  c.flags[5] = 1;
+  c.flags[6] = (a.trace_on == 1 && !c.flags[0])
+                   ? (int)__hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : 0;
+  c.flags[7] = (int)(u32)wall_clock64();
+  if (c.t.trig >= 0 && !c.flags[0]) {
+    const int sub = (c.agent >= 0 ? c.agent : (int)blockIdx.x) & (kSubCounters - 1);
+    __hip_atomic_fetch_add(gp(a.counters + ((size_t)c.t.trig * kSubCounters + sub) * kCounterStride), 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 DEV void finish(Ctx& c) {
   const StepArgs& a = *c.a;
   __syncthreads();
   if (threadIdx.x == 0) {
+    trigger_event(c);
     if (a.trace_on && !c.flags[0]) {
       // ticketed trace: global tickets and append order; timing trace: clocks
-      // only, one slot per task id (no returning atomics on the task's path)
+      // only, one slot per task id (no returning atomics on the task's path).
+      // The end ticket and clock are the trigger's.
       const bool tk = a.trace_on == 1;
-      u32 te = tk ? __hip_atomic_fetch_add(a.status + ST_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       u32 slot = tk ? __hip_atomic_fetch_add(a.status + ST_TRACE_N, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                     : (u32)c.id;
       if (slot < (u32)a.geom->n_tasks) {
@@ -303,18 +322,13 @@ DEV void finish(Ctx& c) {
         r.worker = (int16_t)c.agent;
         r.xcc = (int16_t)(__builtin_amdgcn_s_getreg(6164) & 0xF);  // HW_REG_XCC_ID[3:0]
         r.t_start = (u32)c.flags[2];
-        r.t_end = te;
+        r.t_end = (u32)c.flags[6];
         r.dep_seen = (u32)c.flags[1];
         r.step = a.epoch;
         r.clk_start = (u32)c.flags[3];
-        r.clk_end = (u32)wall_clock64();
+        r.clk_end = (u32)c.flags[7];
         a.trace[slot] = r;
       }
-    }
-    if (c.t.trig >= 0 && !c.flags[0]) {
-      const int sub = (c.agent >= 0 ? c.agent : (int)blockIdx.x) & (kSubCounters - 1);
-      __hip_atomic_fetch_add(gp(a.counters + ((size_t)c.t.trig * kSubCounters + sub) * kCounterStride), 1u,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -366,6 +380,38 @@ DEV void body_embed(Ctx& c, const OpDesc& op) {
 // issued ahead of the rest of the weight ring: in-order load completion would
 // otherwise make the input wait behind the whole ring.
 constexpr int kStageCH = 8;  // tagged words in flight per thread
+
+// Words p[k0 + i*stride] (i < N, index < K) loaded as w[i]: while any of them
+// still carries an older step's tag (its producer may trigger before storing,
+// see gemv_valu), re-read the whole batch at agent scope, one round trip per
+// retry, bounded by the watchdog budget.
+template <int N>
+DEV void refresh_batch(u64 (&w)[N], const u64* p, int k0, int stride, int K, const StepArgs& a) {
+  auto stale = [&]() {
+    bool st = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (k0 + i * stride < K && (u32)(w[i] >> 32) != a.tag) st = true;
+    return st;
+  };
+  if (!stale()) return;
+  const u64 t0 = wall_clock64();
+  for (int it = 0;; ++it) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      w[i] = __hip_atomic_load(gp(p + min(k0 + i * stride, K - 1)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!stale()) return;
+    if ((it & 7) == 7 && (__hip_atomic_load(a.status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+                          wall_clock64() - t0 > a.budget)) {
+      // report through the word-level slow path (records the address, aborts)
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (k0 + i * stride < K && (u32)(w[i] >> 32) != a.tag) w[i] = ld_t_slow(p + k0 + i * stride, a.tag, a.budget, a.status);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
 struct StageFirst {
   u64 w[kStageCH];
   float g[kStageCH];
@@ -404,11 +450,12 @@ DEV void stage_finish(Ctx& c, const OpDesc& op, int tid, const StageFirst& f, fl
 #pragma unroll
         for (int i = 0; i < CH; ++i) gv[i] = op.norm_in ? ldg(op.g + min(k0 + tid + i * NT, K - 1)) : 1.0f;
       }
+      refresh_batch<CH>(w, in, k0 + tid, NT, K, a);
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int k = k0 + tid + i * NT;
         if (k < K) {
-          const float v = fix_t(w[i], in + k, a);
+          const float v = __uint_as_float((u32)w[i]);
           xs[b * K + k] = v * gv[i];
           ss[b] += v * v;
         }
@@ -487,6 +534,7 @@ DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 r
 // input words goes out, then the rest of the ring, then the input is staged
 // while the ring streams.  Loads go through a buffer resource so that
 // out-of-range segments return zeros without touching memory.
+constexpr int kEarlySegments = 2;  // segments of wavefront 0 still to consume when an early trigger fires
 template <int NB, int S, int LOADS>
 DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   constexpr int DEPTH = LOADS / S > 1 ? LOADS / S : 2;
@@ -497,7 +545,10 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
   const int nrw = NR > wave ? (NR - wave + NWAVE - 1) / NWAVE : 0;
   const int NSEG = nrw * SPR;
-  const int PRE = min(DEPTH, (op.pre + S - 1) / S);  // ring segments issued before the wait
+  // ring segments issued before the wait; a control wavefront (op.pad & 1)
+  // issues none, so that its event polls do not complete behind weight data
+  const int PRE = ((op.pad & 1) && wave == 0) ? 0 : min(DEPTH, (op.pre + S - 1) / S);
+  const bool early = (op.pad & 2) != 0;  // trigger before the epilogue (tagged outputs)
   const uint16_t* Wt = op.w + (size_t)(u32)t.a3;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, (int)((u32)NR * (u32)K * 2u), 0x00020000);
@@ -585,6 +636,10 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
 #pragma unroll
       for (int u = 0; u < S; ++u) buf[d][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff(fi, fq, u), 0, AUX_NT);
       if (++fq == SPR) { fq = 0; ++fi; }
+      // early trigger: once wavefront 0 has kEarlySegments segments left to
+      // consume, the outputs are about an event hop away; consumers that
+      // read first find older tags and re-read (refresh_batch / fix_t)
+      if (early && wave == 0 && s0 + d + kEarlySegments >= NSEG && threadIdx.x == 0) trigger_event(c);
     }
   }
   __syncthreads();

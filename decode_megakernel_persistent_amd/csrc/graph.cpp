@@ -957,7 +957,7 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   if (batch <= 0 || batch > 16) return bad("batch must be in 1..16");
   if (cap <= 0 || cap > (1 << 20)) return bad("max_ctx out of range");
   if (workers <= 0 || workers > 4096) return bad("worker count out of range");
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (o.reserved[i]) return bad("reserved options must be zero");
   if (o.prefetch_loads < 0 || o.prefetch_loads > 64) return bad("prefetch_loads must be in 0..64");
   if (o.trace < 0 || o.trace > 2) return bad("trace must be 0, 1 or 2");

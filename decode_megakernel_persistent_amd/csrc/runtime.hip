@@ -40,6 +40,7 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
   c.lds = lds;
   c.flags = flags;
   c.pos = pos;
+  if (threadIdx.x == 0) flags[5] = 0;  // not triggered yet (read after the body's barriers)
   const OpDesc& op = a.ops[c.t.op];
   switch (op.kind) {
     case OP_QKV:
@@ -182,6 +183,7 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
       c.lds = nullptr;
       c.flags = flags;
       c.pos = nullptr;
+      if (threadIdx.x == 0) flags[5] = 0;
       wait_dep(c);
       if (flags[0]) return;
       route_wave(a, a.ops[c.t.op], threadIdx.x);
@@ -377,6 +379,17 @@ static bool swizzle16(const CopyJob& cj, const mk_tensor* t, const char* src, ch
 // issue blocks once the compute unit's outstanding-miss capacity is full, so
 // a deep pre-wait burst delays the wait and the input staging behind data
 // that then sits in registers; a short burst lets staging overlap the stream.
+// GEMV producers whose tasks trigger once their last weight loads are issued
+// (before the epilogue stores): their consumers read tagged words and re-read
+// stale ones, so an early trigger overlaps the event hop with the tail of the
+// producing task.
+static bool early_trigger_kinds(int32_t kind) {
+  return kind == OP_QKV || kind == OP_OPROJ || kind == OP_GATEUP || kind == OP_DOWN || kind == OP_ROUTER;
+}
+static bool ctrl_wave_kinds(int32_t kind) {
+  (void)kind;
+  return false;
+}
 static int32_t default_prefetch_loads(int32_t kind) {
   (void)kind;
   return 64;  // the whole ring
@@ -492,6 +505,7 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
     d.norm_in = o.norm_in;
     d.ntasks = o.ntasks;
     d.pre = G.opts.prefetch_loads > 0 ? G.opts.prefetch_loads : default_prefetch_loads(o.kind);
+    d.pad = (ctrl_wave_kinds(o.kind) ? 1 : 0) | (early_trigger_kinds(o.kind) && !G.opts.late_trigger ? 2 : 0);
     d.w = o.w_off >= 0 ? (const uint16_t*)(arena + o.w_off) : nullptr;
     d.g = o.g_off >= 0 ? (const float*)(arena + o.g_off) : nullptr;
     d.g2 = o.g2_off >= 0 ? (const float*)(arena + o.g2_off) : nullptr;

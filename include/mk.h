@@ -100,7 +100,10 @@ typedef struct {
                               MK_ERR_ARG when the graph has dispatcher tasks (routed experts). */
   int32_t prefetch_loads;  /* GEMV weight loads per lane (16 bytes each) issued before a task's
                               dependency wait; 0 = per-operator default */
-  int32_t reserved[5];     /* must be zero */
+  int32_t late_trigger;    /* 1 = GEMV tasks trigger their event after storing their outputs;
+                              0 = once their last weight loads are issued (consumers re-read
+                              words whose step tag is not yet current; default) */
+  int32_t reserved[4];     /* must be zero */
 } mk_build_opts;
 
 /* One logical tensor handed to mk_load_weights.  Names:
