@@ -918,7 +918,7 @@ DEV float group_reduce(float v, int Lc) {
 // (the split-KV combine of flash decoding).  Lc lanes (C rounded up to a power
 // of two) share one output, one chunk per lane: one batch of loads, then three
 // group reductions.
-DEV void merge_slice(Ctx& c, const u64* parts, u64* out, int b, int gi, int k0, int n) {
+DEV void merge_slice(Ctx& c, const u64* parts, u64* out, int b, int gi, int k0, int n, bool early = false) {
   const StepArgs& a = *c.a;
   const Geom& G = *a.geom;
   const int D = G.D, NG = G.G, C = G.C;
@@ -943,6 +943,8 @@ DEV void merge_slice(Ctx& c, const u64* parts, u64* out, int b, int gi, int k0, 
       lse = fix_t(wl, pl, a);
       o = fix_t(wo, pl + 2 + d, a);
     }
+    // inputs of the last pass are current: the outputs are a few instructions away
+    if (early && (p + 1) * per_pass >= n && tid == 0) trigger_event(c);
     const float M = group_reduce<true>(lse, Lc);
     const float w = lse == -INFINITY ? 0.f : expf(lse - M);
     const float num = group_reduce<false>(w * o, Lc);
@@ -952,7 +954,7 @@ DEV void merge_slice(Ctx& c, const u64* parts, u64* out, int b, int gi, int k0, 
 }
 
 DEV void body_merge(Ctx& c, const OpDesc& op) {
-  merge_slice(c, op.in, op.out, c.t.a0, c.t.a1, c.t.a2, c.t.a3);
+  merge_slice(c, op.in, op.out, c.t.a0, c.t.a1, c.t.a2, c.t.a3, (op.pad & 2) != 0);
 }
 
 // ---------------------------------------------------------------- attention
@@ -1145,6 +1147,9 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
   }
   __syncthreads();
 
+  // early trigger (separate merge tasks only): the partials are the output
+  // pass and the stores away; merge tasks that read first re-read stale words
+  if ((op.pad & 2) && !op.aux && tid == 0) trigger_event(c);
   // o[h][2 columns] = sum over this lane's rows of p[r][h] V_r
   float o[NG][2];
 #pragma unroll

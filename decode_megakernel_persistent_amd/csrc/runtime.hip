@@ -379,12 +379,14 @@ static bool swizzle16(const CopyJob& cj, const mk_tensor* t, const char* src, ch
 // issue blocks once the compute unit's outstanding-miss capacity is full, so
 // a deep pre-wait burst delays the wait and the input staging behind data
 // that then sits in registers; a short burst lets staging overlap the stream.
-// GEMV producers whose tasks trigger once their last weight loads are issued
-// (before the epilogue stores): their consumers read tagged words and re-read
-// stale ones, so an early trigger overlaps the event hop with the tail of the
-// producing task.
+// Producers whose tasks trigger before their outputs are stored (GEMV tiles
+// once their last weight loads are issued, attention chunks after their
+// softmax, merge slices once their inputs are current): consumers read tagged
+// words and re-read stale ones, so an early trigger overlaps the event hop
+// with the tail of the producing task.
 static bool early_trigger_kinds(int32_t kind) {
-  return kind == OP_QKV || kind == OP_OPROJ || kind == OP_GATEUP || kind == OP_DOWN || kind == OP_ROUTER;
+  return kind == OP_QKV || kind == OP_OPROJ || kind == OP_GATEUP || kind == OP_DOWN || kind == OP_ROUTER ||
+         kind == OP_ATTN || kind == OP_MERGE;
 }
 static bool ctrl_wave_kinds(int32_t kind) {
   (void)kind;
