@@ -118,7 +118,11 @@ constexpr int kScoreFloats = 8192;       // attention scores of one chunk (32 KB
 
 enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT = 1, ERR_CONFIG = 2, ERR_BAD_TASK = 3, ERR_BAD_INPUT = 4, ERR_NOT_RESIDENT = 5 };
 
-// VGPR cap of the worker kernel: 2 x 248 + 8 (one dispatch wavefront) <= 512 per SIMD.
+// Register hint of the worker kernel.  amdgpu_num_vgpr counts the unified
+// VGPR + AGPR file on this architecture, so it does not bind the 256
+// architectural registers; what must hold is that two worker wavefronts and
+// the dispatch wavefront (about 64 registers: it also routes MoE tokens) fit
+// a SIMD's 512, which mk_load_weights checks on the built kernels.
 constexpr int kWorkerVgprs = 248;
 
 }  // namespace mk
