@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--workload", default="qwen3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lpt", action="store_true")
+    ap.add_argument("--multi-steps", type=int, default=16,
+                    help="also time mk_decode_steps with this many greedy steps per launch (0 = skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-only", action="store_true", help="persistent steps only (for profilers)")
     ap.add_argument("--no-watchdog", action="store_true",
@@ -194,6 +196,32 @@ def main():
         print(f"[bench] launch-per-task: mean {mean_l:.4f} ms/step", file=sys.stderr, flush=True)
         sess.set_mode(mk.MK_PERSISTENT)
 
+    multi = None
+    n_multi = min(args.multi_steps, cap - int(pos0.max()))
+    if n_multi > 1:
+        # the whole greedy loop on the device: n_multi steps per launch, tokens
+        # fed back from the lm_head argmax; events bracket only the launch
+        sess.set_kv(kv_k, kv_v)
+        sess.tokens.copy_(tok_dev[0])
+        sess.positions.copy_(torch.as_tensor(pos0.astype(np.int32), device=sess.device))
+        out_tok = torch.empty((n_multi, B), dtype=torch.int32, device=sess.device)
+        st = torch.cuda.current_stream()
+        reps = 4
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps + 1)]
+        for r in range(reps + 1):  # the first launch is a warmup
+            ev[r][0].record(st)
+            mk.mk_decode_steps(sess.g, sess.tokens.data_ptr(), sess.positions.data_ptr(), sess.kv,
+                               sess.logits.data_ptr(), out_tok.data_ptr(), n_multi, sess.stream)
+            ev[r][1].record(st)
+        torch.cuda.synchronize()
+        sess.check()
+        t_m = [a.elapsed_time(b) for a, b in ev[1:]]
+        per = statistics.fmean(t_m) / n_multi
+        multi = {"steps_per_launch": n_multi, "launches": reps, "ms_per_step": round(per, 4),
+                 "ms_per_token": round(per / B, 4), "tokens_per_s": round(B * 1000.0 / per, 2),
+                 "speedup_vs_one_step_launches": round(mean / per, 4)}
+        print(f"[bench] multi-step: {n_multi} steps per launch, {per:.4f} ms/step", file=sys.stderr, flush=True)
+
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC) and args.workload == "qwen3-8b" and B == 1:
         from decode_megakernel_persistent_amd import profsum
@@ -237,6 +265,7 @@ def main():
                      "algorithmic_bytes_per_launch": round(bytes_mean), "kernel": "mk_worker",
                      "launch_ms": round(mean, 4)},
         "launch_per_task": lpt,
+        "multi_step": multi,
         "cpu_baseline": cpu,
         "tokens_per_s": round(B * 1000.0 / mean, 2),
     }

@@ -113,6 +113,7 @@ def lib():
                               ctypes.POINTER(ctypes.c_size_t)],
         "mk_load_weights": [_vp, ctypes.POINTER(mk_tensor), ctypes.c_int32, _vp, _vp, _vp, _vp],
         "mk_decode_step": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, _vp],
+        "mk_decode_steps": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, _vp, ctypes.c_int32, _vp],
         "mk_set_mode": [_vp, ctypes.c_int32, ctypes.c_int32],
         "mk_check": [_vp],
         "mk_read_trace": [_vp, _vp, ctypes.c_int64, _i64p],
@@ -141,7 +142,8 @@ def lib():
     return L
 
 
-EXPORTED = ["mk_build_graph", "mk_workspace_size", "mk_load_weights", "mk_decode_step", "mk_set_mode", "mk_check",
+EXPORTED = ["mk_build_graph", "mk_workspace_size", "mk_load_weights", "mk_decode_step", "mk_decode_steps",
+            "mk_set_mode", "mk_check",
             "mk_read_trace", "mk_check_trace", "mk_read_counters", "mk_simulate", "mk_graph_stats", "mk_dump_graph",
             "mk_get_tasks", "mk_get_events", "mk_get_worker_lists", "mk_get_raw_edges", "mk_destroy_graph",
             "mk_last_error", "mk_hip_runtime_path"]
@@ -222,6 +224,12 @@ def mk_load_weights(g: int, tensors: Sequence[Tuple[str, object]], d_arena: int,
 
 def mk_decode_step(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int, stream: int = 0):
     _chk(lib().mk_decode_step(g, d_tokens, d_positions, ctypes.byref(kv), d_logits, stream or None), "mk_decode_step")
+
+
+def mk_decode_steps(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int, d_tokens_out: int,
+                    n_steps: int, stream: int = 0):
+    _chk(lib().mk_decode_steps(g, d_tokens, d_positions, ctypes.byref(kv), d_logits, d_tokens_out or None, n_steps,
+                               stream or None), "mk_decode_steps")
 
 
 def mk_set_mode(g: int, mode: int, per_task_launch: int = 0):
@@ -374,6 +382,18 @@ class Session:
         mk_decode_step(self.g, self.tokens.data_ptr(), self.positions.data_ptr(), self.kv, self.logits.data_ptr(),
                        self.stream)
         self.steps += 1
+
+    def decode(self, tokens, positions, n_steps: int):
+        """Enqueue n_steps greedy steps in one persistent launch, starting from
+        tokens at positions; returns the device tensor [n_steps, B] of greedy
+        tokens (valid after sync).  self.logits holds the last step's logits."""
+        self.tokens.copy_(torch.as_tensor(np.asarray(tokens, dtype=np.int32).reshape(self.batch)))
+        self.positions.copy_(torch.as_tensor(np.asarray(positions, dtype=np.int32).reshape(self.batch)))
+        out = torch.full((n_steps, self.batch), -1, dtype=torch.int32, device=self.device)
+        mk_decode_steps(self.g, self.tokens.data_ptr(), self.positions.data_ptr(), self.kv, self.logits.data_ptr(),
+                        out.data_ptr(), n_steps, self.stream)
+        self.steps += n_steps
+        return out
 
     def set_mode(self, mode: int, per_task_launch: int = 0):
         mk_set_mode(self.g, mode, per_task_launch)

@@ -56,6 +56,11 @@ struct StepArgs {
   int32_t trace_on;
   int32_t lpt_first;  // launch-per-task: first task id of the launch
   int32_t n_workers;
+  int32_t n_steps;    // decode steps of this launch (persistent mode); epoch and tag advance by one per step
+  u32 run_base;       // persistent steps before this launch: workers count one arrival / completion per step
+  int32_t step;       // this step's index within the launch
+  int32_t* tokens_out;  // [n_steps][B] greedy tokens, or null
+  u64* cand;          // lm_head tile candidates [tile][B] x (value, id), tagged
 };
 
 // Thread index behind an empty asm: index math derived from it stays inside
@@ -354,11 +359,98 @@ DEV void block_sum(float (&v)[NB], float* red) {
 }
 
 // ---------------------------------------------------------------- embedding
+// Greedy tokens from the lm_head candidates of an earlier step of this
+// launch: wavefront 0 waits until the lm_head event has counted need *
+// done_epoch triggers (that step's tiles), then all threads reduce the tiles'
+// candidates, tagged `tag`, to one id per sequence b in [b0, b1) (ties to the
+// lower id).  Results in tok[b] (LDS), valid after the final barrier.
+DEV void lm_argmax(Ctx& c, u32 done_epoch, u32 tag, int b0, int b1, int* tok) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int ev = G.lm_event, T = G.lm_tiles, B = G.B;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  if (tid < 64) {
+    const u32 target = (u32)a.events[ev].need * done_epoch;
+    const u64 t0 = wall_clock64();
+    for (int it = 0;; ++it) {
+      const u32 seen = event_total(a, ev, lane);
+      if (seen >= target) break;
+      if ((it & 7) == 7 && (__hip_atomic_load(a.status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+                            wall_clock64() - t0 > a.budget)) {
+        if (lane == 0) {
+          report_timeout(a, c.id, ev, seen, target);
+          c.flags[0] = 1;
+        }
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  float* sv = (float*)c.lds + 256;  // [NWAVE][16] values (tok[] may sit below)
+  int* si = (int*)(sv + NWAVE * 16);
+  for (int b = b0; b < b1; ++b) {
+    float best = -INFINITY;
+    int id = 0x7fffffff;
+    if (!c.flags[0]) {
+      for (int j = tid; j < T; j += NT) {
+        const u64* p = a.cand + ((size_t)j * B + b) * 2;
+        u64 wv = ld_raw(p), wi = ld_raw(p + 1);
+        if ((u32)(wv >> 32) != tag) wv = ld_t_slow(p, tag, a.budget, a.status);
+        if ((u32)(wi >> 32) != tag) wi = ld_t_slow(p + 1, tag, a.budget, a.status);
+        const float v = __uint_as_float((u32)wv);
+        const int i = (int)(u32)wi;
+        if (v > best || (v == best && i < id)) {
+          best = v;
+          id = i;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(best, o);
+      const int oi = __shfl_xor(id, o);
+      if (ov > best || (ov == best && oi < id)) {
+        best = ov;
+        id = oi;
+      }
+    }
+    if (lane == 0) {
+      sv[wave * 16 + (b - b0)] = best;
+      si[wave * 16 + (b - b0)] = id;
+    }
+  }
+  __syncthreads();
+  if (tid >= b0 && tid < b1) {
+    float best = sv[tid - b0];
+    int id = si[tid - b0];
+    for (int w = 1; w < NWAVE; ++w) {
+      const float v = sv[w * 16 + tid - b0];
+      const int i = si[w * 16 + tid - b0];
+      if (v > best || (v == best && i < id)) {
+        best = v;
+        id = i;
+      }
+    }
+    tok[tid] = id;
+  }
+  __syncthreads();
+}
+
 DEV void body_embed(Ctx& c, const OpDesc& op) {
   const StepArgs& a = *c.a;
   const Geom& G = *a.geom;
   const int b = c.t.a0, H = G.H;
-  int tok = a.tokens[b];
+  int tok;
+  if (a.step > 0) {
+    // token feedback: the previous step's greedy token, recorded for the caller
+    int* tk = (int*)c.lds;
+    lm_argmax(c, a.epoch, a.tag - 1u, b, b + 1, tk);
+    tok = tk[b];
+    if (threadIdx.x == 0 && a.tokens_out) a.tokens_out[(size_t)(a.step - 1) * G.B + b] = tok;
+  } else {
+    tok = a.tokens[b];
+  }
   if (tok < 0 || tok >= G.V) {
     if (threadIdx.x == 0) {
       u32 z = 0;
@@ -492,6 +584,64 @@ DEV u64 gemv_residual_prefetch(const Ctx& c, const OpDesc& op, int NB) {
   if ((op.kind != OP_OPROJ && op.kind != OP_DOWN) || j >= NB * nr) return 0ull;
   const int b = j / nr, row = c.t.a1 + (j - b * nr);
   return ld_raw(op.res + (size_t)b * op.N + row);
+}
+
+// Where a finished GEMV tile leaves its per-row results and per-sequence
+// norm scales in LDS (VALU path, batch NB; MFMA path).
+DEV const float* valu_rows(const Ctx& c) { return (const float*)c.lds + kStageFloats; }
+DEV const float* valu_scales(const Ctx& c, int NB) { return (const float*)(c.flags + 8) + NB * NWAVE; }
+
+// Greedy candidates of one lm_head tile: per sequence, the largest logit of
+// the tile's rows and its vocabulary id (ties to the lower id), taken from the
+// same fp32 values the epilogue stores, kept as two tagged words.  All
+// threads, after the barrier that ends the dot products (the input staging
+// area at the start of LDS is dead by then and holds the per-wave results).
+DEV void lm_candidates(Ctx& c, const float* rsl, int NR, const float* rn, int NB) {
+  const StepArgs& a = *c.a;
+  const int nr = c.t.a2, r0 = c.t.a1, tile = c.t.a0, B = a.geom->B;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  float* sv = (float*)c.lds;          // [NWAVE][16] values
+  int* si = (int*)(sv + NWAVE * 16);  // [NWAVE][16] ids
+  for (int b = 0; b < NB; ++b) {
+    float best = -INFINITY;
+    int id = 0x7fffffff;
+    for (int r = tid; r < nr; r += NT) {
+      const float v = rsl[b * NR + r] * rn[b];
+      if (v > best) {  // rows ascend per thread: the first maximum is kept
+        best = v;
+        id = r0 + r;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(best, o);
+      const int oi = __shfl_xor(id, o);
+      if (ov > best || (ov == best && oi < id)) {
+        best = ov;
+        id = oi;
+      }
+    }
+    if (lane == 0) {
+      sv[wave * 16 + b] = best;
+      si[wave * 16 + b] = id;
+    }
+  }
+  __syncthreads();
+  if (tid < NB) {
+    float best = sv[tid];
+    int id = si[tid];
+    for (int w = 1; w < NWAVE; ++w) {
+      const float v = sv[w * 16 + tid];
+      const int i = si[w * 16 + tid];
+      if (v > best || (v == best && i < id)) {
+        best = v;
+        id = i;
+      }
+    }
+    u64* p = a.cand + ((size_t)tile * B + tid) * 2;
+    st_t(p, best, a.tag);
+    st_t(p + 1, __int_as_float(id), a.tag);
+  }
 }
 
 DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 res0, const float* rn, int NB) {
@@ -755,6 +905,10 @@ DEV void mfma_stage(Ctx& c, const OpDesc& op, int tid, int c0, int KBc, char* xf
     }
   }
 }
+
+// LDS locations of the MFMA path's per-row results [B][NR] and norm scales [16].
+DEV const float* mfma_rows(const Ctx& c) { return (const float*)(c.lds + 2 * (kMfmaKC / 32 * 1024)); }
+DEV const float* mfma_scales(const Ctx& c) { return mfma_rows(c) + kRowResultFloats + NWAVE * 256 + 16 * NWAVE; }
 
 DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
   const StepArgs& a = *c.a;

@@ -534,6 +534,20 @@ bool finish_graph(Graph& g, std::string* err) {
   }
   for (int32_t e = 0; e < (int32_t)ev_prod.size(); ++e)
     for (int32_t u : ev_prod[e]) ttrig[u].push_back(e);
+  // Terminal event of the logits: the lm_head tiles trigger it and no task of
+  // the step waits on it; a multi-step launch waits on it before embedding the
+  // next step's tokens, and its count checks that every tile ran.
+  int32_t lm_raw_event = -1;
+  {
+    std::vector<int32_t> lm;
+    for (int32_t t = 0; t < n0; ++t)
+      if (g.raw[t].op >= 0 && g.ops[g.raw[t].op].kind == OP_LMHEAD && ttrig[t].empty()) lm.push_back(t);
+    if (!lm.empty()) {
+      lm_raw_event = (int32_t)ev_prod.size();
+      ev_prod.push_back(lm);
+      for (int32_t u : lm) ttrig[u].push_back(lm_raw_event);
+    }
+  }
 
   // ---- normalisation
   auto new_empty = [&](int32_t dep, int32_t trig) {
@@ -622,6 +636,8 @@ bool finish_graph(Graph& g, std::string* err) {
     *err = "unreachable event";
     return false;
   }
+  g.lm_event = lm_raw_event >= 0 ? ev_new[lm_raw_event] : -1;
+  g.lm_tiles = lm_raw_event >= 0 ? (int32_t)ev_prod[lm_raw_event].size() : 0;
   g.events.assign(ne, Event{});
   for (int32_t e = 0; e < ne; ++e) {
     Event& ev = g.events[ev_new[e]];
@@ -903,6 +919,8 @@ void layout(Graph& g) {
     b.off = sc;
     sc = align_up(sc + b.words * 8, 256);
   }
+  g.off_cand = sc;  // greedy candidates of the lm_head tiles: [tile][B] x (value, id) tagged words
+  sc = align_up(sc + (int64_t)std::max(1, g.lm_tiles) * g.B * 2 * 8, 256);
   g.scratch_bytes = sc;
   g.trace_bytes = g.opts.trace ? (int64_t)g.tasks.size() * (int64_t)sizeof(mk_trace_rec) : 0;
 }
@@ -1029,6 +1047,8 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   ge.L = s.n_layers;
   ge.C = g->C;
   ge.mfma = g->gemv == MK_GEMV_MFMA ? 1 : 0;
+  ge.lm_event = g->lm_event;
+  ge.lm_tiles = g->lm_tiles;
   ge.cap = cap;
   ge.E = s.n_experts;
   ge.topk = s.top_k;

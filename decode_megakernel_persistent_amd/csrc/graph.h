@@ -72,12 +72,13 @@ struct Graph {
   std::vector<int32_t> launch_first, launch_count;  // launch-per-task ranges (BFS order)
   std::vector<std::pair<int32_t, int32_t>> raw_edges;  // (producer, consumer) task ids
   int64_t n_empty = 0, n_reduced_edges = 0;
+  int32_t lm_event = -1, lm_tiles = 0;  // terminal event of the lm_head tiles, and their count
 
   // layout
   std::vector<CopyJob> copies;
   int64_t arena_bytes = 0, scratch_bytes = 0, trace_bytes = 0;
   int64_t off_geom = 0, off_ops = 0, off_tasks = 0, off_events = 0, off_wloff = 0, off_wlids = 0, off_invfreq = 0;
-  int64_t off_counters = 0, off_status = 0, off_progress = 0, off_arrive = 0, off_state_end = 0;
+  int64_t off_counters = 0, off_status = 0, off_progress = 0, off_arrive = 0, off_state_end = 0, off_cand = 0;
   int64_t weight_bytes_step = 0;
 };
 
@@ -126,6 +127,7 @@ struct mk_graph {
   int32_t mode = 0, per_task_launch = 0, device = -1;
   bool loaded = false;
   uint32_t epoch = 0;  // steps whose events counted since the last reset
+  uint32_t persistent_steps = 0;  // of those, steps run by persistent launches (worker arrival/done counts)
   uint32_t tag = 1;    // data tag of the next step
   uint64_t budget_ticks = 0;
 };

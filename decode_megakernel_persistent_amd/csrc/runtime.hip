@@ -29,7 +29,7 @@
 namespace mk {
 
 // ---------------------------------------------------------------- kernels
-template <int NB>
+template <int NB, bool MULTI>
 DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int* flags, const int* pos) {
   Ctx c;
   c.a = &a;
@@ -81,6 +81,14 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
       wait_dep(c);
       break;
   }
+  // greedy candidates of an lm_head tile, from the row results still in LDS
+  // (one copy of this code per kernel, not one per GEMV shape)
+  if constexpr (MULTI) {
+    if (op.kind == OP_LMHEAD && a.cand) {
+      if constexpr (NB == kMfmaVariant) lm_candidates(c, mfma_rows(c), c.t.a2, mfma_scales(c), a.geom->B);
+      else lm_candidates(c, valu_rows(c), c.t.a2, valu_scales(c, NB), NB);
+    }
+  }
   finish(c);
 }
 
@@ -107,25 +115,78 @@ DEV bool entry_ok(const StepArgs& a, int* flags, int* pos) {
 // Register cap: two worker wavefronts per SIMD must leave room for the
 // dispatch wavefront (8 VGPRs) on whichever CU it runs, or the worker
 // workgroup of that CU could not become resident.
-template <int NB>
+// Two variants: MULTI = false runs one step (the plain task loop); MULTI =
+// true runs a.n_steps greedy steps, with the lm_head argmax candidates and the
+// token feedback.  Separate instantiations keep the outer step loop and the
+// candidate code out of the one-step kernel, where they measurably slowed the
+// bodies (register and instruction-cache pressure, ~1.3% of a step).
+template <int NB, bool MULTI>
 __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerVgprs))) mk_worker(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flags[64];
   __shared__ int pos[16];
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.status + ST_ARRIVED, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // arrival and completion count one per step, so that the dispatch
+  // wavefront's targets (workers x persistent steps so far) hold for any mix
+  // of launch lengths
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(a.status + ST_ARRIVED, (u32)a.n_steps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (entry_ok(a, flags, pos)) {
     const int w = blockIdx.x;
-    for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
-      if (threadIdx.x == 0)
-        __hip_atomic_store(a.progress + w, (u32)a.wl_ids[k] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      run_task<NB>(a, a.wl_ids[k], w, false, lds, flags, pos);
-      __syncthreads();
-      if (flags[0]) break;
+    if constexpr (!MULTI) {
+      for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
+        if (threadIdx.x == 0)
+          __hip_atomic_store(a.progress + w, (u32)a.wl_ids[k] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        run_task<NB, false>(a, a.wl_ids[k], w, false, lds, flags, pos);
+        __syncthreads();
+        if (flags[0]) break;
+      }
+    } else {
+      // Multi-step decode: the same task list once per step, with the step's
+      // epoch (event targets), data tag and positions, advanced in the
+      // kernel's own argument copy.  A step's embedding waits on the previous
+      // step's lm_head event, so a worker may run ahead into the next step
+      // only as far as the events allow.
+      const int n = a.n_steps;
+      for (int s = 0; s < n; ++s) {
+        if (s > 0) {
+          if ((int)threadIdx.x < a.geom->B) pos[threadIdx.x] = a.positions[threadIdx.x] + s;
+          __syncthreads();
+        }
+        for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
+          if (threadIdx.x == 0)
+            __hip_atomic_store(a.progress + w, (u32)a.wl_ids[k] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          run_task<NB, true>(a, a.wl_ids[k], w, false, lds, flags, pos);
+          __syncthreads();
+          if (flags[0]) break;
+        }
+        if (flags[0]) break;
+        if (s + 1 < n) {
+          a.epoch += 1u;
+          a.tag += 1u;
+          a.step += 1;
+        }
+      }
+      // the last step's greedy tokens
+      if (a.tokens_out && w == 0 && !flags[0] && a.geom->lm_event >= 0) {
+        Ctx c;
+        c.a = &a;
+        c.id = -1;
+        c.agent = w;
+        c.lpt = false;
+        c.lds = lds;
+        c.flags = flags;
+        c.pos = pos;
+        int* tk = (int*)lds;
+        lm_argmax(c, a.epoch + 1u, a.tag, 0, a.geom->B, tk);
+        if ((int)threadIdx.x < a.geom->B && !flags[0])
+          a.tokens_out[(size_t)(n - 1) * a.geom->B + threadIdx.x] = tk[threadIdx.x];
+      }
     }
     if (threadIdx.x == 0 && !flags[0])
       __hip_atomic_store(a.progress + w, 0xFFFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.status + ST_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(a.status + ST_DONE, (u32)a.n_steps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NB>
@@ -133,7 +194,7 @@ __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flags[64];
   __shared__ int pos[16];
-  if (entry_ok(a, flags, pos)) run_task<NB>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags, pos);
+  if (entry_ok(a, flags, pos)) run_task<NB, false>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags, pos);
 }
 
 // The dispatch wavefront: runs the dispatcher's own task list (work-list
@@ -142,7 +203,9 @@ __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
 // watchdog budget.
 __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
   const int W = a.n_workers;
-  const u32 target = (u32)W * (a.epoch + 1u);
+  // launch-per-task steps advance the epoch but not the workers' arrival and
+  // completion counts, so the targets count persistent steps only
+  const u32 target = (u32)W * (a.run_base + (u32)a.n_steps);
   u64 t0 = wall_clock64();
   // entry handshake: every worker workgroup must become resident while the
   // others wait for it; give it a short budget, then report and abort
@@ -170,25 +233,32 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
     __shared__ int flags[64];
     if (threadIdx.x < 64) flags[threadIdx.x] = 0;
     __syncthreads();
-    for (int k = a.wl_off[W]; k < a.wl_off[W + 1]; ++k) {
-      const int id = a.wl_ids[k];
-      if (threadIdx.x == 0)
-        __hip_atomic_store(a.progress + W, (u32)id + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      Ctx c;
-      c.a = &a;
-      c.t = a.tasks[id];
-      c.id = id;
-      c.agent = W;
-      c.lpt = false;
-      c.lds = nullptr;
-      c.flags = flags;
-      c.pos = nullptr;
-      if (threadIdx.x == 0) flags[5] = 0;
-      wait_dep(c);
-      if (flags[0]) return;
-      route_wave(a, a.ops[c.t.op], threadIdx.x);
-      finish(c);
-      __syncthreads();
+    const u32 epoch0 = a.epoch, tag0 = a.tag;
+    for (int s = 0; s < a.n_steps; ++s) {
+      StepArgs& as = a;
+      as.epoch = epoch0 + (u32)s;
+      as.tag = tag0 + (u32)s;
+      as.step = s;
+      for (int k = a.wl_off[W]; k < a.wl_off[W + 1]; ++k) {
+        const int id = a.wl_ids[k];
+        if (threadIdx.x == 0)
+          __hip_atomic_store(a.progress + W, (u32)id + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        Ctx c;
+        c.a = &as;
+        c.t = a.tasks[id];
+        c.id = id;
+        c.agent = W;
+        c.lpt = false;
+        c.lds = nullptr;
+        c.flags = flags;
+        c.pos = nullptr;
+        if (threadIdx.x == 0) flags[5] = 0;
+        wait_dep(c);
+        if (flags[0]) return;
+        route_wave(as, a.ops[c.t.op], threadIdx.x);
+        finish(c);
+        __syncthreads();
+      }
     }
     if (threadIdx.x == 0)
       __hip_atomic_store(a.progress + W, 0xFFFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -198,7 +268,7 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
     u32 done = __hip_atomic_load(a.status + ST_DONE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done >= target) break;
     if (__hip_atomic_load(a.status + ST_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-    if (wall_clock64() - t0 > 4 * a.budget) {
+    if (wall_clock64() - t0 > (u64)(3 + a.n_steps) * a.budget) {
       if (threadIdx.x == 0) report_timeout(a, -1, -1, done, target);
       break;
     }
@@ -210,13 +280,22 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
 // (any batch up to 16).  Separate instantiations keep each one's register
 // allocation to the GEMV it actually runs.
 typedef void (*kernel_fn)(StepArgs);
-static const void* worker_fn(int v) {
+static const void* worker_fn(int v, bool multi) {
+  if (multi) {
+    switch (v) {
+      case 1: return (const void*)mk_worker<1, true>;
+      case 2: return (const void*)mk_worker<2, true>;
+      case 3: return (const void*)mk_worker<3, true>;
+      case 4: return (const void*)mk_worker<4, true>;
+      default: return (const void*)mk_worker<kMfmaVariant, true>;
+    }
+  }
   switch (v) {
-    case 1: return (const void*)mk_worker<1>;
-    case 2: return (const void*)mk_worker<2>;
-    case 3: return (const void*)mk_worker<3>;
-    case 4: return (const void*)mk_worker<4>;
-    default: return (const void*)mk_worker<kMfmaVariant>;
+    case 1: return (const void*)mk_worker<1, false>;
+    case 2: return (const void*)mk_worker<2, false>;
+    case 3: return (const void*)mk_worker<3, false>;
+    case 4: return (const void*)mk_worker<4, false>;
+    default: return (const void*)mk_worker<kMfmaVariant, false>;
   }
 }
 static const void* lpt_fn(int v) {
@@ -537,14 +616,16 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   const int64_t us = G.opts.spin_timeout_us > 0 ? G.opts.spin_timeout_us : 2000000;
   g->budget_ticks = (uint64_t)us * (uint64_t)(wcr > 0 ? wcr : 100000) / 1000ull;
   for (int v : {1, 2, 3, 4, (int)kMfmaVariant}) {
-    (void)hipFuncSetAttribute(worker_fn(v), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    (void)hipFuncSetAttribute(worker_fn(v, false), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    (void)hipFuncSetAttribute(worker_fn(v, true), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     (void)hipFuncSetAttribute(lpt_fn(v), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   }
   (void)hipGetLastError();
   // co-residency: two worker wavefronts per SIMD plus the dispatch wavefront
-  {
+  // (both the one-step and the multi-step worker kernel)
+  for (bool multi : {false, true}) {
     hipFuncAttributes fw, fd;
-    HIPCHK(hipFuncGetAttributes(&fw, worker_fn(kernel_variant(G))));
+    HIPCHK(hipFuncGetAttributes(&fw, worker_fn(kernel_variant(G), multi)));
     HIPCHK(hipFuncGetAttributes(&fd, (const void*)mk_dispatch));
     auto gran = [](int v) { return (v + 7) / 8 * 8; };
     if (2 * gran(fw.numRegs) + gran(fd.numRegs) > 512 || fw.localSizeBytes > 0) {
@@ -558,6 +639,7 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   g->trace = d_trace;
   g->loaded = true;
   g->epoch = 0;
+  g->persistent_steps = 0;
   g->tag = 1;
   return MK_OK;
 }
@@ -574,6 +656,11 @@ mk_status mk_set_mode(mk_graph* g, int32_t mode, int32_t per_task_launch) {
 
 mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
                          float* d_logits, void* stream_) {
+  return mk_decode_steps(g, d_tokens, d_positions, kv, d_logits, nullptr, 1, stream_);
+}
+
+mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
+                          float* d_logits, int32_t* d_tokens_out, int32_t n_steps, void* stream_) {
   if (!g || !g->G) {
     set_error("mk_decode_step: null graph");
     return MK_ERR_ARG;
@@ -587,6 +674,19 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
     return MK_ERR_ARG;
   }
   Graph& G = *g->G;
+  if (n_steps < 1 || n_steps > kMaxStepsPerLaunch) {
+    set_error("mk_decode_steps: n_steps must be in 1.." + std::to_string(kMaxStepsPerLaunch));
+    return MK_ERR_ARG;
+  }
+  if ((n_steps > 1 || d_tokens_out) && g->mode != MK_PERSISTENT) {
+    set_error("mk_decode_steps: several steps per launch and token output need the persistent mode");
+    return MK_ERR_ARG;
+  }
+  if (n_steps > 1 && G.opts.trace) {
+    set_error("mk_decode_steps: the task trace holds one step; build without trace for several steps per launch");
+    return MK_ERR_ARG;
+  }
+  if (g->tag > 0xFFFFFFFFu - (uint32_t)n_steps) g->tag = 1;  // tags of this launch stay nonzero
   if (kv->capacity != G.cap) {
     set_error("mk_decode_step: kv capacity " + std::to_string(kv->capacity) + " differs from the graph's max_ctx " +
               std::to_string(G.cap));
@@ -618,6 +718,11 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
   a.magic = G.geom.magic;
   a.trace_on = G.opts.trace;
   a.n_workers = G.W;
+  a.n_steps = n_steps;
+  a.run_base = g->persistent_steps;
+  a.step = 0;
+  a.tokens_out = d_tokens_out;
+  a.cand = (u64*)(scratch + G.off_cand);
   const int nb = kernel_variant(G);
   if (a.trace_on == 1) HIPCHK(hipMemsetAsync(a.status + ST_TICKET, 0, 2 * sizeof(u32), stream));
   if (g->mode == MK_PERSISTENT) {
@@ -629,7 +734,8 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
     // slower.
     if (watch) HIPCHK(hipEventRecord((hipEvent_t)g->ev_a, stream));
     void* kargs[] = {&a};
-    hipError_t e = hipLaunchCooperativeKernel(worker_fn(nb), dim3(G.W), dim3(NT), kargs, kLdsBytes, stream);
+    const bool multi = n_steps > 1 || d_tokens_out != nullptr;
+    hipError_t e = hipLaunchCooperativeKernel(worker_fn(nb, multi), dim3(G.W), dim3(NT), kargs, kLdsBytes, stream);
     if (e == hipErrorCooperativeLaunchTooLarge) {
       (void)hipGetLastError();
       set_error("mk_decode_step: " + std::to_string(G.W) + " workers cannot be co-resident on this device");
@@ -663,8 +769,9 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
       }
     }
   }
-  g->epoch += 1;
-  g->tag += 1;
+  g->epoch += (uint32_t)n_steps;
+  if (g->mode == MK_PERSISTENT) g->persistent_steps += (uint32_t)n_steps;
+  g->tag += (uint32_t)n_steps;
   if (g->tag == 0) g->tag = 1;
   return MK_OK;
 }
@@ -749,6 +856,7 @@ mk_status mk_check(mk_graph* g) {
   const u32 none = 0xFFFFFFFFu;
   HIPCHK(hipMemcpy((char*)g->scratch + G.off_status + ST_MIN_TASK * 4, &none, 4, hipMemcpyHostToDevice));
   g->epoch = 0;
+  g->persistent_steps = 0;
   set_error("mk_check: " + msg);
   return rc;
 }

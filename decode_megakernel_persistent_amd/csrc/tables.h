@@ -83,6 +83,8 @@ struct Geom {
   float attn_scale;     // 1/sqrt(D)
   uint32_t magic;       // configuration hash checked by every worker at entry
   int32_t mfma;         // 1: GEMV tiles use the MFMA path (swizzled weight fragments)
+  int32_t lm_event;     // terminal event of the lm_head tiles (-1: none)
+  int32_t lm_tiles;     // lm_head tiles (producers of lm_event)
   const double* inv_freq;  // RoPE inverse frequencies [D/2]
 };
 
@@ -124,5 +126,8 @@ enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT = 1, ERR_CONFIG = 2, ERR_BAD
 // the dispatch wavefront (about 64 registers: it also routes MoE tokens) fit
 // a SIMD's 512, which mk_load_weights checks on the built kernels.
 constexpr int kWorkerVgprs = 248;
+
+// Decode steps one persistent launch may run (mk_decode_steps).
+constexpr int kMaxStepsPerLaunch = 4096;
 
 }  // namespace mk

@@ -186,6 +186,25 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
 mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
                          float* d_logits, void* stream);
 
+/* Greedy decode of n_steps steps in ONE persistent launch: the whole decode
+ * loop inside the megakernel, as the MPK pages' single mpk() call runs the
+ * generation (survey page on MPK, section 5, the demo's decode loop).
+ * Step 0 embeds d_tokens[B] at d_positions[B]; step s > 0 embeds the greedy
+ * token of step s-1 (argmax of its fp32 logits, ties to the lower id) at
+ * d_positions[b] + s.  The argmax is reduced on the device from per-tile
+ * candidates of the lm_head; the next step's embedding waits for the previous
+ * step's lm_head event.  d_tokens_out[n_steps][B] (int32, device, nullable
+ * when n_steps == 1) receives every step's greedy token; d_logits[B][V] holds
+ * the last step's logits.  Caller-owned buffers; d_tokens and d_positions are
+ * not modified.  Needs 0 <= d_positions[b] + n_steps - 1 < capacity (else the
+ * step reports MK_ERR_TIMEOUT / bad input through mk_check), the persistent
+ * mode, and a graph built without trace when n_steps > 1.
+ * Errors: as mk_decode_step; MK_ERR_ARG for n_steps outside 1..4096, for
+ * token output or n_steps > 1 in launch-per-task mode, or for n_steps > 1
+ * with a trace. */
+mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
+                          float* d_logits, int32_t* d_tokens_out, int32_t n_steps, void* stream);
+
 /* Switch the execution mode of a loaded graph (same tables and arena). */
 mk_status mk_set_mode(mk_graph* g, int32_t mode, int32_t per_task_launch);
 

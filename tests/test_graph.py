@@ -141,8 +141,10 @@ def test_8b_graph_shape_counts(merge_tasks, merges, merge_events):
         assert st.tasks == 1 + 36 * (256 * 5 + merges) + 256
         assert st.empty_tasks == 0
         # per layer: 8 QKV head groups, (8 chunk groups), attention/merge -> O, O, gate-up, down
-        assert st.events == 36 * (12 + merge_events) + 1
-        assert st.launches_per_step == st.events + 1
+        # plus the embedding event and the terminal event of the lm_head tiles
+        assert st.events == 36 * (12 + merge_events) + 2
+        # one launch per consumer range (the lm_head event has none) plus the roots
+        assert st.launches_per_step == (st.events - 1) + 1
         assert st.max_tasks_per_worker <= 36 * (5 + (merges + 255) // 256) + 2
         assert abs(st.weight_bytes / 1e9 - 15.137) < 0.01
     finally:
