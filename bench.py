@@ -194,6 +194,26 @@ def main():
                "persistent_speedup": round(mean_l / mean, 3),
                "overhead_share": round(1.0 - mean / mean_l, 4)}
         print(f"[bench] launch-per-task: mean {mean_l:.4f} ms/step", file=sys.stderr, flush=True)
+        # the same launches captured once into a HIP graph and replayed: what
+        # remains of the gap to the persistent kernel is not host launch cost
+        h = sess.capture_lpt_graph()
+        st = torch.cuda.current_stream()
+        pos_t = torch.as_tensor(pos0.astype(np.int32), device=sess.device)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.warmup + args.steps)]
+        for i in range(args.warmup + args.steps):
+            sess.tokens.copy_(tok_dev[i % tok_dev.shape[0]])
+            sess.positions.copy_(pos_t + i)
+            ev[i][0].record(st)
+            sess.replay_lpt_graph(h)
+            ev[i][1].record(st)
+        torch.cuda.synchronize()
+        sess.check()
+        t_g = [a.elapsed_time(b) for a, b in ev[args.warmup:]]
+        mean_g = statistics.fmean(t_g)
+        lpt["graph_ms_per_step"] = round(mean_g, 4)
+        lpt["graph_persistent_speedup"] = round(mean_g / mean, 3)
+        print(f"[bench] launch-per-task as a HIP graph: mean {mean_g:.4f} ms/step", file=sys.stderr, flush=True)
         sess.set_mode(mk.MK_PERSISTENT)
 
     multi = None

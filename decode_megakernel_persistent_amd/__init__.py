@@ -114,6 +114,8 @@ def lib():
         "mk_load_weights": [_vp, ctypes.POINTER(mk_tensor), ctypes.c_int32, _vp, _vp, _vp, _vp],
         "mk_decode_step": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, _vp],
         "mk_decode_steps": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, _vp, ctypes.c_int32, _vp],
+        "mk_capture_lpt_graph": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, ctypes.POINTER(_vp)],
+        "mk_lpt_graph_launch": [_vp, _vp],
         "mk_set_mode": [_vp, ctypes.c_int32, ctypes.c_int32],
         "mk_check": [_vp],
         "mk_read_trace": [_vp, _vp, ctypes.c_int64, _i64p],
@@ -134,6 +136,8 @@ def lib():
         f.restype = ctypes.c_int32
     L.mk_destroy_graph.argtypes = [_vp]
     L.mk_destroy_graph.restype = None
+    L.mk_lpt_graph_destroy.argtypes = [_vp]
+    L.mk_lpt_graph_destroy.restype = None
     L.mk_last_error.restype = ctypes.c_char_p
     L.mk_last_error.argtypes = []
     L.mk_hip_runtime_path.restype = ctypes.c_char_p
@@ -143,7 +147,7 @@ def lib():
 
 
 EXPORTED = ["mk_build_graph", "mk_workspace_size", "mk_load_weights", "mk_decode_step", "mk_decode_steps",
-            "mk_set_mode", "mk_check",
+            "mk_capture_lpt_graph", "mk_lpt_graph_launch", "mk_lpt_graph_destroy", "mk_set_mode", "mk_check",
             "mk_read_trace", "mk_check_trace", "mk_read_counters", "mk_simulate", "mk_graph_stats", "mk_dump_graph",
             "mk_get_tasks", "mk_get_events", "mk_get_worker_lists", "mk_get_raw_edges", "mk_destroy_graph",
             "mk_last_error", "mk_hip_runtime_path"]
@@ -224,6 +228,21 @@ def mk_load_weights(g: int, tensors: Sequence[Tuple[str, object]], d_arena: int,
 
 def mk_decode_step(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int, stream: int = 0):
     _chk(lib().mk_decode_step(g, d_tokens, d_positions, ctypes.byref(kv), d_logits, stream or None), "mk_decode_step")
+
+
+def mk_capture_lpt_graph(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int) -> int:
+    out = _vp()
+    _chk(lib().mk_capture_lpt_graph(g, d_tokens, d_positions, ctypes.byref(kv), d_logits, ctypes.byref(out)),
+         "mk_capture_lpt_graph")
+    return out.value
+
+
+def mk_lpt_graph_launch(lg: int, stream: int = 0):
+    _chk(lib().mk_lpt_graph_launch(lg, stream or None), "mk_lpt_graph_launch")
+
+
+def mk_lpt_graph_destroy(lg: int):
+    lib().mk_lpt_graph_destroy(lg)
 
 
 def mk_decode_steps(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int, d_tokens_out: int,
@@ -336,6 +355,9 @@ class Session:
         self.steps = 0
 
     def close(self):
+        for h in getattr(self, "_lpt_graphs", []):
+            mk_lpt_graph_destroy(h)
+        self._lpt_graphs = []
         if getattr(self, "g", None):
             mk_destroy_graph(self.g)
             self.g = None
@@ -394,6 +416,19 @@ class Session:
                         out.data_ptr(), n_steps, self.stream)
         self.steps += n_steps
         return out
+
+    def capture_lpt_graph(self) -> int:
+        """Capture one launch-per-task step on this session's buffers into a HIP
+        graph; replay with replay_lpt_graph after writing tokens/positions."""
+        torch.cuda.synchronize(self.device)
+        h = mk_capture_lpt_graph(self.g, self.tokens.data_ptr(), self.positions.data_ptr(), self.kv,
+                                 self.logits.data_ptr())
+        self._lpt_graphs = getattr(self, "_lpt_graphs", []) + [h]
+        return h
+
+    def replay_lpt_graph(self, h: int):
+        mk_lpt_graph_launch(h, self.stream)
+        self.steps += 1
 
     def set_mode(self, mode: int, per_task_launch: int = 0):
         mk_set_mode(self.g, mode, per_task_launch)

@@ -367,6 +367,65 @@ int device_cu_count() {
   return p.multiProcessorCount;
 }
 
+// Kernel arguments of one launch (epoch and tag taken from the graph handle).
+StepArgs step_args(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
+                   float* d_logits, int32_t* d_tokens_out, int32_t n_steps) {
+  Graph& G = *g->G;
+  char* arena = (char*)g->arena;
+  char* scratch = (char*)g->scratch;
+  StepArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.geom = (const Geom*)(arena + G.off_geom);
+  a.ops = (const OpDesc*)(arena + G.off_ops);
+  a.tasks = (const Task*)(arena + G.off_tasks);
+  a.events = (const Event*)(arena + G.off_events);
+  a.wl_off = (const int32_t*)(arena + G.off_wloff);
+  a.wl_ids = (const int32_t*)(arena + G.off_wlids);
+  a.counters = (u32*)(scratch + G.off_counters);
+  a.status = (u32*)(scratch + G.off_status);
+  a.progress = (u32*)(scratch + G.off_progress);
+  a.tokens = d_tokens;
+  a.positions = d_positions;
+  a.kv_k = (uint16_t*)kv->k;
+  a.kv_v = (uint16_t*)kv->v;
+  a.logits = d_logits;
+  a.trace = (mk_trace_rec*)g->trace;
+  a.budget = g->budget_ticks;
+  a.epoch = g->epoch;
+  a.tag = g->tag;
+  a.magic = G.geom.magic;
+  a.trace_on = G.opts.trace;
+  a.n_workers = G.W;
+  a.n_steps = n_steps;
+  a.run_base = g->persistent_steps;
+  a.step = 0;
+  a.tokens_out = d_tokens_out;
+  a.cand = (u64*)(scratch + G.off_cand);
+  return a;
+}
+
+// The launch-per-task sequence of one step on `stream`: one mk_lpt launch per
+// (event range, operator) in BFS order, or one per task.
+mk_status launch_lpt(mk_graph* g, StepArgs a, hipStream_t stream) {
+  Graph& G = *g->G;
+  const void* fn = lpt_fn(kernel_variant(G));
+  for (size_t i = 0; i < G.launch_first.size(); ++i) {
+    const int32_t first = G.launch_first[i], count = G.launch_count[i];
+    if (g->per_task_launch) {
+      for (int32_t k = 0; k < count; ++k) {
+        a.lpt_first = first + k;
+        void* kargs[] = {&a};
+        HIPCHK(hipLaunchKernel(fn, dim3(1), dim3(NT), kargs, kLdsBytes, stream));
+      }
+    } else {
+      a.lpt_first = first;
+      void* kargs[] = {&a};
+      HIPCHK(hipLaunchKernel(fn, dim3(count), dim3(NT), kargs, kLdsBytes, stream));
+    }
+  }
+  return MK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -686,43 +745,15 @@ mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d
     set_error("mk_decode_steps: the task trace holds one step; build without trace for several steps per launch");
     return MK_ERR_ARG;
   }
-  if (g->tag > 0xFFFFFFFFu - (uint32_t)n_steps) g->tag = 1;  // tags of this launch stay nonzero
+  // tags of this launch stay nonzero and below kGraphTag (reserved for graph replays)
+  if (g->tag > kGraphTag - 1u - (uint32_t)n_steps) g->tag = 1;
   if (kv->capacity != G.cap) {
     set_error("mk_decode_step: kv capacity " + std::to_string(kv->capacity) + " differs from the graph's max_ctx " +
               std::to_string(G.cap));
     return MK_ERR_ARG;
   }
   hipStream_t stream = (hipStream_t)stream_;
-  char* arena = (char*)g->arena;
-  char* scratch = (char*)g->scratch;
-  StepArgs a;
-  std::memset(&a, 0, sizeof a);
-  a.geom = (const Geom*)(arena + G.off_geom);
-  a.ops = (const OpDesc*)(arena + G.off_ops);
-  a.tasks = (const Task*)(arena + G.off_tasks);
-  a.events = (const Event*)(arena + G.off_events);
-  a.wl_off = (const int32_t*)(arena + G.off_wloff);
-  a.wl_ids = (const int32_t*)(arena + G.off_wlids);
-  a.counters = (u32*)(scratch + G.off_counters);
-  a.status = (u32*)(scratch + G.off_status);
-  a.progress = (u32*)(scratch + G.off_progress);
-  a.tokens = d_tokens;
-  a.positions = d_positions;
-  a.kv_k = (uint16_t*)kv->k;
-  a.kv_v = (uint16_t*)kv->v;
-  a.logits = d_logits;
-  a.trace = (mk_trace_rec*)g->trace;
-  a.budget = g->budget_ticks;
-  a.epoch = g->epoch;
-  a.tag = g->tag;
-  a.magic = G.geom.magic;
-  a.trace_on = G.opts.trace;
-  a.n_workers = G.W;
-  a.n_steps = n_steps;
-  a.run_base = g->persistent_steps;
-  a.step = 0;
-  a.tokens_out = d_tokens_out;
-  a.cand = (u64*)(scratch + G.off_cand);
+  StepArgs a = step_args(g, d_tokens, d_positions, kv, d_logits, d_tokens_out, n_steps);
   const int nb = kernel_variant(G);
   if (a.trace_on == 1) HIPCHK(hipMemsetAsync(a.status + ST_TICKET, 0, 2 * sizeof(u32), stream));
   if (g->mode == MK_PERSISTENT) {
@@ -753,27 +784,88 @@ mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d
       HIPCHK(hipStreamWaitEvent(stream, (hipEvent_t)g->ev_b, 0));
     }
   } else {
-    const void* fn = lpt_fn(nb);
-    for (size_t i = 0; i < G.launch_first.size(); ++i) {
-      const int32_t first = G.launch_first[i], count = G.launch_count[i];
-      if (g->per_task_launch) {
-        for (int32_t k = 0; k < count; ++k) {
-          a.lpt_first = first + k;
-          void* kargs[] = {&a};
-          HIPCHK(hipLaunchKernel(fn, dim3(1), dim3(NT), kargs, kLdsBytes, stream));
-        }
-      } else {
-        a.lpt_first = first;
-        void* kargs[] = {&a};
-        HIPCHK(hipLaunchKernel(fn, dim3(count), dim3(NT), kargs, kLdsBytes, stream));
-      }
-    }
+    const mk_status rc = launch_lpt(g, a, stream);
+    if (rc != MK_OK) return rc;
   }
   g->epoch += (uint32_t)n_steps;
   if (g->mode == MK_PERSISTENT) g->persistent_steps += (uint32_t)n_steps;
   g->tag += (uint32_t)n_steps;
   if (g->tag == 0) g->tag = 1;
   return MK_OK;
+}
+
+struct mk_lpt_graph {
+  mk_graph* g = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+mk_status mk_capture_lpt_graph(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions,
+                               const mk_kv_cache* kv, float* d_logits, mk_lpt_graph** out) {
+  if (!out) {
+    set_error("mk_capture_lpt_graph: null output");
+    return MK_ERR_ARG;
+  }
+  *out = nullptr;
+  if (!g || !g->G || !g->loaded) {
+    set_error("mk_capture_lpt_graph: weights not loaded");
+    return MK_ERR_STATE;
+  }
+  if (!d_tokens || !d_positions || !kv || !kv->k || !kv->v || !d_logits || kv->capacity != g->G->cap) {
+    set_error("mk_capture_lpt_graph: bad argument");
+    return MK_ERR_ARG;
+  }
+  if (g->G->opts.trace) {
+    // the ticketed trace clears its counters with a memset, which a captured graph must not hold
+    set_error("mk_capture_lpt_graph: build the graph without trace");
+    return MK_ERR_ARG;
+  }
+  StepArgs a = step_args(g, d_tokens, d_positions, kv, d_logits, nullptr, 1);
+  a.tag = kGraphTag;  // replays write and accept only this tag; stream order makes it safe
+  hipStream_t cs;
+  HIPCHK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  mk_status rc = MK_OK;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    set_error("mk_capture_lpt_graph: hipStreamBeginCapture failed");
+    rc = MK_ERR_HIP;
+  } else {
+    rc = launch_lpt(g, a, cs);
+    const hipError_t e = hipStreamEndCapture(cs, &graph);
+    if (rc == MK_OK && e != hipSuccess) {
+      set_error(std::string("mk_capture_lpt_graph: hipStreamEndCapture: ") + hipGetErrorString(e));
+      rc = MK_ERR_HIP;
+    }
+  }
+  if (rc == MK_OK && hipGraphInstantiateWithFlags(&exec, graph, 0) != hipSuccess) {
+    set_error("mk_capture_lpt_graph: hipGraphInstantiate failed");
+    rc = MK_ERR_HIP;
+  }
+  if (graph) (void)hipGraphDestroy(graph);
+  (void)hipStreamDestroy(cs);
+  if (rc != MK_OK) return rc;
+  mk_lpt_graph* lg = new mk_lpt_graph();
+  lg->g = g;
+  lg->exec = exec;
+  *out = lg;
+  return MK_OK;
+}
+
+mk_status mk_lpt_graph_launch(mk_lpt_graph* lg, void* stream) {
+  if (!lg || !lg->exec || !lg->g || !lg->g->loaded) {
+    set_error("mk_lpt_graph_launch: bad graph");
+    return MK_ERR_ARG;
+  }
+  HIPCHK(hipGraphLaunch(lg->exec, (hipStream_t)stream));
+  // the replayed tasks trigger their events like any launch-per-task step
+  lg->g->epoch += 1;
+  return MK_OK;
+}
+
+void mk_lpt_graph_destroy(mk_lpt_graph* lg) {
+  if (!lg) return;
+  if (lg->exec) (void)hipGraphExecDestroy(lg->exec);
+  delete lg;
 }
 
 mk_status mk_check(mk_graph* g) {

@@ -130,4 +130,7 @@ constexpr int kWorkerVgprs = 248;
 // Decode steps one persistent launch may run (mk_decode_steps).
 constexpr int kMaxStepsPerLaunch = 4096;
 
+// Data tag of captured launch-per-task graphs (never used by other steps).
+constexpr uint32_t kGraphTag = 0xFFFFFFFFu;
+
 }  // namespace mk

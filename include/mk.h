@@ -205,6 +205,28 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
 mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
                           float* d_logits, int32_t* d_tokens_out, int32_t n_steps, void* stream);
 
+/* Launch-per-task mode captured once into a HIP graph and replayed: the same
+ * task bodies and launch sequence as mode MK_LAUNCH_PER_TASK, without the
+ * host's per-launch cost.  This is the pages' CUDA-Graphs comparison point for
+ * the megakernel (MPK blog, the overhead of kernel launches that graphs do
+ * not remove; survey page on MPK, section 5).
+ *   mk_capture_lpt_graph: records one step's launches (the graph's
+ *     per_task_launch setting) with the given device buffers baked in; the
+ *     caller rewrites d_tokens / d_positions between replays.  Needs a graph
+ *     built without trace (its trace clears counters with a memset).
+ *     *out receives the handle, owned by the caller.
+ *   mk_lpt_graph_launch: one step, asynchronous on `stream`.  Replays use a
+ *     data tag reserved for them, and count as steps for the graph's event
+ *     epochs, so persistent steps may follow.
+ *   mk_lpt_graph_destroy: frees the handle; the mk_graph must outlive it.
+ * Errors: MK_ERR_STATE (not loaded), MK_ERR_ARG (bad argument, trace on),
+ * MK_ERR_HIP. */
+typedef struct mk_lpt_graph mk_lpt_graph;
+mk_status mk_capture_lpt_graph(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions,
+                               const mk_kv_cache* kv, float* d_logits, mk_lpt_graph** out);
+mk_status mk_lpt_graph_launch(mk_lpt_graph* lg, void* stream);
+void mk_lpt_graph_destroy(mk_lpt_graph* lg);
+
 /* Switch the execution mode of a loaded graph (same tables and arena). */
 mk_status mk_set_mode(mk_graph* g, int32_t mode, int32_t per_task_launch);
 
