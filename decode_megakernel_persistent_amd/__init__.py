@@ -22,15 +22,27 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmk.so")
 
 
-def source_hash() -> str:
-    """Hash of the sources the device kernels and their tables are built from
-    (ties profiler counters to the kernels they were taken on)."""
+def source_hash(csrc: Optional[str] = None) -> str:
+    """Hash of the sources the device kernels and their task tables are built
+    from (ties profiler counters to the kernels they were taken on).  Of
+    runtime.hip only the kernel part counts: its host section (the C ABI, from
+    the line that opens it) launches the kernels but does not change what they
+    read or write."""
     import hashlib
     h = hashlib.sha256()
     for f in ("device.h", "runtime.hip", "graph.cpp", "graph.h", "tables.h"):
-        with open(os.path.join(_PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc or os.path.join(_PKG, "csrc"), f), "rb") as fh:
+            data = fh.read()
+        if f == "runtime.hip":
+            cut = data.find(HOST_SECTION_MARKER)
+            if cut < 0:
+                raise RuntimeError("runtime.hip: host section marker not found")
+            data = data[:cut]
+        h.update(data)
     return h.hexdigest()[:16]
+
+
+HOST_SECTION_MARKER = b"// ==================================================================== host"
 
 MK_OK = 0
 MK_ERR_ARG = -1

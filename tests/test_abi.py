@@ -87,3 +87,21 @@ def test_workspace_sizes_and_stats():
         assert st.gemv == mk.MK_GEMV_VALU
     finally:
         mk.mk_destroy_graph(g)
+
+
+def test_source_hash_tracks_kernels_not_host_code(tmp_path):
+    # profiler counters are tied to the kernels through this hash: an edit of
+    # the C-ABI host section keeps it, an edit of device code changes it
+    import shutil
+    src = os.path.join(ROOT, "decode_megakernel_persistent_amd", "csrc")
+    d = tmp_path / "csrc"
+    shutil.copytree(src, d)
+    h0 = mk.source_hash(str(d))
+    assert h0 == mk.source_hash()
+    rt = (d / "runtime.hip").read_text()
+    assert mk.HOST_SECTION_MARKER.decode() in rt
+    (d / "runtime.hip").write_text(rt + "\n// host-side comment\n")
+    assert mk.source_hash(str(d)) == h0
+    dev = (d / "device.h").read_text()
+    (d / "device.h").write_text(dev + "\n// device-side comment\n")
+    assert mk.source_hash(str(d)) != h0
