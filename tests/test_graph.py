@@ -227,3 +227,27 @@ def test_dump_graph_json(tmp_path):
         assert d["gemv"] == "valu"
     finally:
         mk.mk_destroy_graph(g)
+
+
+@pytest.mark.parametrize("wname,gemv", [("tiny", mk.MK_GEMV_AUTO), ("qwen3-8b", mk.MK_GEMV_AUTO),
+                                        ("qwen3-8b-b16", mk.MK_GEMV_AUTO)])
+def test_lm_head_terminal_event(wname, gemv):
+    # the lm_head tiles trigger one event that no task of the step waits on;
+    # a multi-step launch waits on it before the next step's embedding
+    w = synth.WORKLOADS[wname]
+    g = mk.mk_build_graph(w.shape, w.batch, w.capacity, mk.make_opts(gemv=gemv))
+    try:
+        tasks, ev = mk.mk_get_tasks(g), mk.mk_get_events(g)
+        lm = np.nonzero(tasks[:, 0] == mk.OP_KINDS.index("lmhead"))[0]
+        trig = set(tasks[lm, 3].tolist())
+        assert len(trig) == 1
+        e = trig.pop()
+        assert e >= 0
+        need, first, last, producers = ev[e]
+        assert need == len(lm) == producers
+        assert last < first  # no consumers
+        assert not np.any(tasks[:, 2] == e)  # nobody depends on it
+        # tiles are numbered 0..n-1 (the candidate buffer's index)
+        assert sorted(tasks[lm, 4].tolist()) == list(range(len(lm)))
+    finally:
+        mk.mk_destroy_graph(g)
