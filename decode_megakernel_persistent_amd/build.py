@@ -2,9 +2,12 @@
 
     python -m decode_megakernel_persistent_amd.build
 
-Every call compiles from scratch: hipcc for the HIP translation unit (device
-code plus the host runtime), g++ for the host-only compiler / simulator /
-checker, linked by hipcc into ``decode_megakernel_persistent_amd/libmk.so``.
+Every call compiles from scratch: hipcc for ``runtime.hip``, once per kernel
+batch variant (``-DMK_UNIT_NB=v``: that variant's worker and launch-per-task
+kernels, the dispatch kernel with v = 1) and once for its host side
+(``-DMK_UNIT_HOST``: the C ABI), all in parallel; g++ for the host-only
+compiler / simulator / checker; linked by hipcc into
+``decode_megakernel_persistent_amd/libmk.so``.
 Also builds a host-only protocol simulator executable under ThreadSanitizer
 (``_build/mk_sim_tsan``) when requested.
 """
@@ -33,6 +36,7 @@ HIP_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-pthread", "-Wall"]
 HOST_SRCS = ["graph.cpp", "sim.cpp"]
+KERNEL_VARIANTS = [1, 2, 3, 4, 16]  # VALU batches 1..4, and the MFMA variant (kMfmaVariant)
 
 
 def _run(cmd, verbose):
@@ -55,10 +59,11 @@ def build(verbose: bool = False, tsan: bool = False) -> str:
         obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
         jobs.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    hobj = os.path.join(BUILD, "runtime.o")
-    jobs.append([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "runtime.hip"), "-o", hobj])
-    objs.append(hobj)
-    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+    for unit in [f"-DMK_UNIT_NB={v}" for v in KERNEL_VARIANTS] + ["-DMK_UNIT_HOST"]:
+        obj = os.path.join(BUILD, "runtime_" + unit.split("-D")[1].replace("=", "") + ".o")
+        jobs.append([HIPCC, *HIP_FLAGS, unit, *inc, "-c", os.path.join(CSRC, "runtime.hip"), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 16)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-pthread", "-ldl"], verbose)

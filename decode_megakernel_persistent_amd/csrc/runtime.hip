@@ -26,6 +26,14 @@
 #include "device.h"
 #include "graph.h"
 
+// Translation units.  The library is compiled from this one file several
+// times in parallel: with MK_UNIT_NB=v, the kernels of batch variant v (and,
+// for v = 1, the dispatch kernel); with MK_UNIT_HOST, the host side, which
+// only declares the kernels.  Without either macro the file is one unit.
+#if !defined(MK_UNIT_NB) && !defined(MK_UNIT_HOST)
+#define MK_UNIT_ALL 1
+#endif
+
 namespace mk {
 
 // ---------------------------------------------------------------- kernels
@@ -197,6 +205,7 @@ __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
   if (entry_ok(a, flags, pos)) run_task<NB, false>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags, pos);
 }
 
+#if defined(MK_UNIT_ALL) || (defined(MK_UNIT_NB) && MK_UNIT_NB == 1)
 // The dispatch wavefront: runs the dispatcher's own task list (work-list
 // routing of routed-expert layers), then watches the workers until every one
 // has finished the step, raising the abort flag if that takes longer than the
@@ -275,7 +284,40 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
     __builtin_amdgcn_s_sleep(127);
   }
 }
+#else
+__global__ void __launch_bounds__(64) mk_dispatch(StepArgs a);
+#endif
 
+#if defined(MK_UNIT_NB)
+// this unit's kernels
+template __global__ void mk_worker<MK_UNIT_NB, false>(StepArgs);
+template __global__ void mk_worker<MK_UNIT_NB, true>(StepArgs);
+template __global__ void mk_lpt<MK_UNIT_NB>(StepArgs);
+#endif
+#if defined(MK_UNIT_HOST)
+// defined in the kernel units
+extern template __global__ void mk_worker<1, false>(StepArgs);
+extern template __global__ void mk_worker<2, false>(StepArgs);
+extern template __global__ void mk_worker<3, false>(StepArgs);
+extern template __global__ void mk_worker<4, false>(StepArgs);
+extern template __global__ void mk_worker<kMfmaVariant, false>(StepArgs);
+extern template __global__ void mk_worker<1, true>(StepArgs);
+extern template __global__ void mk_worker<2, true>(StepArgs);
+extern template __global__ void mk_worker<3, true>(StepArgs);
+extern template __global__ void mk_worker<4, true>(StepArgs);
+extern template __global__ void mk_worker<kMfmaVariant, true>(StepArgs);
+extern template __global__ void mk_lpt<1>(StepArgs);
+extern template __global__ void mk_lpt<2>(StepArgs);
+extern template __global__ void mk_lpt<3>(StepArgs);
+extern template __global__ void mk_lpt<4>(StepArgs);
+extern template __global__ void mk_lpt<kMfmaVariant>(StepArgs);
+#endif
+
+}  // namespace mk
+
+// ==================================================================== host
+#if defined(MK_UNIT_ALL) || defined(MK_UNIT_HOST)
+namespace mk {
 // Kernel variants: 1..4 = VALU GEMV for that batch, kMfmaVariant = MFMA GEMV
 // (any batch up to 16).  Separate instantiations keep each one's register
 // allocation to the GEMV it actually runs.
@@ -311,7 +353,6 @@ static int kernel_variant(const Graph& G) { return G.gemv == MK_GEMV_MFMA ? kMfm
 
 }  // namespace mk
 
-// ==================================================================== host
 using namespace mk;
 
 namespace {
@@ -1113,3 +1154,4 @@ const char* mk_hip_runtime_path(void) {
 }
 
 }  // extern "C"
+#endif  // host section
