@@ -10,7 +10,7 @@
 // Mega-Kernelizing Tensor Programs", abstract; review page 2512.22219, section
 // 2.1: the fused scope is attention + MatMul + RMSNorm).  The pages never
 // write the model's formulas down, so each step below follows the plainest
-// Qwen3 reading; every such reading is listed with its pin in the design doc.
+// Qwen3 reading; each such reading is pinned by a test in tests/test_oracle_pins.py.
 //
 // Arithmetic: IEEE double throughout.  bf16 weights and cache entries are
 // widened exactly.  The only roundings to bf16 are the ones the method itself
