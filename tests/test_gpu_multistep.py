@@ -105,6 +105,18 @@ def test_8b_multistep_matches_single_steps():
     check_multistep(w, harness.prepare(w), 3, oracle_check=False)
 
 
+def test_tied_embedding_multistep():
+    # 0.6B: the lm_head is the embedding matrix (tied), VALU tiles
+    w = synth.WORKLOADS["qwen3-0.6b"]
+    check_multistep(w, harness.prepare(w), 4)
+
+
+def test_8b_batch16_multistep():
+    # 16 ragged sequences on the MFMA tiles: every candidate column in use
+    w = synth.WORKLOADS["qwen3-8b-b16"]
+    check_multistep(w, harness.prepare(w), 2, oracle_check=False)
+
+
 def test_multistep_argument_errors():
     w = synth.WORKLOADS["tiny"]
     prep = harness.prepare(w)
