@@ -197,8 +197,9 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
  * when n_steps == 1) receives every step's greedy token; d_logits[B][V] holds
  * the last step's logits.  Caller-owned buffers; d_tokens and d_positions are
  * not modified.  Needs 0 <= d_positions[b] + n_steps - 1 < capacity (else the
- * step reports MK_ERR_TIMEOUT / bad input through mk_check), the persistent
- * mode, and a graph built without trace when n_steps > 1.
+ * attention bounds check clamps the position and mk_check then reports
+ * MK_ERR_ARG, position out of range), the persistent mode, and a graph built
+ * without trace when n_steps > 1.
  * Errors: as mk_decode_step; MK_ERR_ARG for n_steps outside 1..4096, for
  * token output or n_steps > 1 in launch-per-task mode, or for n_steps > 1
  * with a trace. */
