@@ -88,7 +88,9 @@ class mk_tensor(ctypes.Structure):
 
 
 class mk_kv_cache(ctypes.Structure):
-    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32)]
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("page_table", ctypes.c_void_p), ("n_pages", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class mk_stats(ctypes.Structure):
@@ -133,6 +135,7 @@ def lib():
         "mk_read_trace": [_vp, _vp, ctypes.c_int64, _i64p],
         "mk_check_trace": [_vp, _vp, ctypes.c_int64, ctypes.c_uint32, _u32p],
         "mk_read_counters": [_vp, _u32p, ctypes.c_int64],
+        "mk_read_routing": [_vp, ctypes.c_int32, _i32p, _vp, _vp, ctypes.c_int64],
         "mk_simulate": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
                         _i64p, _u32p],
         "mk_graph_stats": [_vp, ctypes.POINTER(mk_stats)],
@@ -160,7 +163,7 @@ def lib():
 
 EXPORTED = ["mk_build_graph", "mk_workspace_size", "mk_load_weights", "mk_decode_step", "mk_decode_steps",
             "mk_capture_lpt_graph", "mk_lpt_graph_launch", "mk_lpt_graph_destroy", "mk_set_mode", "mk_check",
-            "mk_read_trace", "mk_check_trace", "mk_read_counters", "mk_simulate", "mk_graph_stats", "mk_dump_graph",
+            "mk_read_trace", "mk_check_trace", "mk_read_counters", "mk_read_routing", "mk_simulate", "mk_graph_stats", "mk_dump_graph",
             "mk_get_tasks", "mk_get_events", "mk_get_worker_lists", "mk_get_raw_edges", "mk_destroy_graph",
             "mk_last_error", "mk_hip_runtime_path"]
 
@@ -290,6 +293,19 @@ def mk_read_counters(g: int, n_events: int) -> np.ndarray:
     return out
 
 
+def mk_read_routing(g: int, shape, batch: int, step: int, with_logits: bool = False):
+    """(experts [L,B,K] int32, weights [L,B,K] float32, router logits [L,B,E] float32 or None)
+    of step `step` of the last launch of a routed-expert graph (after sync)."""
+    L, K, E = shape.n_layers, shape.top_k, shape.n_experts
+    e = np.zeros((L, batch, K), dtype=np.int32)
+    w = np.zeros((L, batch, K), dtype=np.float32)
+    rl = np.zeros((L, batch, E), dtype=np.float32) if with_logits else None
+    cap = max(e.size, rl.size if rl is not None else 0)
+    _chk(lib().mk_read_routing(g, step, e.ctypes.data_as(_i32p), w.ctypes.data,
+                               rl.ctypes.data if rl is not None else None, cap), "mk_read_routing")
+    return e, w, rl
+
+
 def mk_simulate(g: int, steps: int = 1, fault: int = 0, timeout_ms: int = 2000, threads: int = 0):
     """(trace records of the last step, final counters) from the host-thread protocol simulator."""
     st = mk_graph_stats(g)
@@ -347,7 +363,11 @@ class Session:
     """One compiled graph plus the caller-owned device buffers it runs on."""
 
     def __init__(self, shape, batch: int, max_ctx: int, opts: Optional[mk_build_opts] = None,
-                 device: str = "cuda:0"):
+                 device: str = "cuda:0", page_size: int = 0, spare_pages: int = 0, page_seed: int = 0):
+        """page_size > 0: a paged KV cache (pools [L][n_pages][Hkv][page_size][D]
+        and a page table [B][max_ctx / page_size]); every sequence's logical
+        pages are spread over the pool by a seeded random permutation, with
+        `spare_pages` pages left unused."""
         self.shape, self.batch, self.max_ctx = shape, batch, max_ctx
         self.device = torch.device(device)
         self.opts = opts or make_opts()
@@ -358,9 +378,25 @@ class Session:
         self.scratch = torch.empty(scratch, dtype=torch.uint8, device=self.device)
         self.trace_buf = torch.empty(max(trace, 1), dtype=torch.uint8, device=self.device) if trace else None
         L, Hkv, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
-        self.k_cache = torch.zeros((L, batch, Hkv, max_ctx, D), dtype=torch.int16, device=self.device)
-        self.v_cache = torch.zeros_like(self.k_cache)
-        self.kv = mk_kv_cache(self.k_cache.data_ptr(), self.v_cache.data_ptr(), max_ctx)
+        self.page_size = page_size
+        if page_size:
+            if max_ctx % page_size:
+                raise ValueError("max_ctx must be a multiple of page_size")
+            pps = max_ctx // page_size
+            self.n_pages = batch * pps + spare_pages
+            perm = np.random.default_rng(page_seed).permutation(self.n_pages)[:batch * pps]
+            self.page_table_host = perm.reshape(batch, pps).astype(np.int32)
+            self.page_table = torch.as_tensor(self.page_table_host, device=self.device)
+            # k_cache / v_cache hold the pools in this mode
+            self.k_cache = torch.zeros((L, self.n_pages, Hkv, page_size, D), dtype=torch.int16, device=self.device)
+            self.v_cache = torch.zeros_like(self.k_cache)
+            self.kv = mk_kv_cache(self.k_cache.data_ptr(), self.v_cache.data_ptr(), max_ctx, page_size,
+                                  self.page_table.data_ptr(), self.n_pages, 0)
+        else:
+            self.n_pages = 0
+            self.k_cache = torch.zeros((L, batch, Hkv, max_ctx, D), dtype=torch.int16, device=self.device)
+            self.v_cache = torch.zeros_like(self.k_cache)
+            self.kv = mk_kv_cache(self.k_cache.data_ptr(), self.v_cache.data_ptr(), max_ctx, 0, None, 0, 0)
         self.tokens = torch.zeros(batch, dtype=torch.int32, device=self.device)
         self.positions = torch.zeros(batch, dtype=torch.int32, device=self.device)
         self.logits = torch.zeros((batch, shape.vocab), dtype=torch.float32, device=self.device)
@@ -400,9 +436,32 @@ class Session:
         del items
 
     def set_kv(self, k: np.ndarray, v: np.ndarray):
-        """Copy host bf16 caches [L][B][Hkv][cap][D] into the device caches."""
-        self.k_cache.copy_(torch.from_numpy(np.ascontiguousarray(k).view(np.int16)))
-        self.v_cache.copy_(torch.from_numpy(np.ascontiguousarray(v).view(np.int16)))
+        """Copy host bf16 caches [L][B][Hkv][cap][D] into the device caches
+        (scattered into their pages when the cache is paged)."""
+        for dst, src in ((self.k_cache, k), (self.v_cache, v)):
+            t = torch.from_numpy(np.ascontiguousarray(src).view(np.int16))
+            if not self.page_size:
+                dst.copy_(t)
+                continue
+            L, B, Hkv, cap, D = t.shape
+            P = self.page_size
+            pages = t.reshape(L, B, Hkv, cap // P, P, D).permute(0, 1, 3, 2, 4, 5).reshape(L, B * (cap // P), Hkv, P, D)
+            dst[:, torch.as_tensor(self.page_table_host.reshape(-1), dtype=torch.long, device=self.device)] = \
+                pages.to(self.device)
+
+    def kv_contiguous(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        """The caches as device tensors [L][B][Hkv][cap][D] (gathered from their pages when paged)."""
+        if not self.page_size:
+            return self.k_cache, self.v_cache
+        L, B, P = self.shape.n_layers, self.batch, self.page_size
+        idx = torch.as_tensor(self.page_table_host.reshape(-1), dtype=torch.long, device=self.device)
+        out = []
+        for pool in (self.k_cache, self.v_cache):
+            g = pool[:, idx]  # [L][B*pps][Hkv][P][D]
+            Hkv, D = g.shape[2], g.shape[4]
+            out.append(g.reshape(L, B, self.max_ctx // P, Hkv, P, D).permute(0, 1, 3, 2, 4, 5)
+                       .reshape(L, B, Hkv, self.max_ctx, D))
+        return out[0], out[1]
 
     def step(self, tokens, positions):
         """Enqueue one decode step; returns the device logits tensor [B, V] (valid after sync)."""
@@ -456,6 +515,29 @@ class Session:
     def read_counters(self) -> np.ndarray:
         torch.cuda.synchronize(self.device)
         return mk_read_counters(self.g, self.stats.events)
+
+    def read_routing(self, step: int = 0, with_logits: bool = True):
+        """Expert choice (and, for the launch's last step, router logits) of step
+        `step` of the last launch: see mk_read_routing."""
+        torch.cuda.synchronize(self.device)
+        return mk_read_routing(self.g, self.shape, self.batch, step, with_logits)
+
+    def kv_rows(self, positions) -> Tuple[np.ndarray, np.ndarray]:
+        """Host copies of the K and V cache rows at positions[b] of every
+        layer, sequence and kv head: two bf16 arrays [L][B][Hkv][D] (uint16)."""
+        torch.cuda.synchronize(self.device)
+        p = np.asarray(positions, dtype=np.int64).reshape(self.batch)
+        if self.page_size:
+            P = self.page_size
+            bi = torch.as_tensor(self.page_table_host[np.arange(self.batch), p // P].astype(np.int64), device=self.device)
+            pos = torch.as_tensor(p % P, device=self.device)
+        else:
+            bi = torch.arange(self.batch, device=self.device)
+            pos = torch.as_tensor(p, device=self.device)
+        # advanced indices split by a slice: the (sequence, row) axis comes first, [B][L][Hkv][D]
+        k = self.k_cache[:, bi, :, pos, :].permute(1, 0, 2, 3)
+        v = self.v_cache[:, bi, :, pos, :].permute(1, 0, 2, 3)
+        return (k.contiguous().cpu().numpy().view(np.uint16), v.contiguous().cpu().numpy().view(np.uint16))
 
     def check_trace(self, recs: np.ndarray, step: int, counters: Optional[np.ndarray] = None):
         mk_check_trace(self.g, recs, step, counters)

@@ -45,8 +45,11 @@ struct StepArgs {
   u32* progress;   // per agent: 1 + id of the current task, 0xFFFFFFFF when done
   const int32_t* tokens;
   const int32_t* positions;
-  uint16_t* kv_k;
+  uint16_t* kv_k;     // contiguous [L][B][Hkv][cap][D], or paged pools [L][n_pages][Hkv][page][D]
   uint16_t* kv_v;
+  const int32_t* page_table;  // paged: physical page of each logical page, [B][cap >> page_shift]
+  int32_t page_shift;         // log2(page size), or -1 for the contiguous layout
+  int32_t n_pages;            // paged: pages per pool
   float* logits;
   mk_trace_rec* trace;
   u64 budget;       // wall-clock ticks any single wait may take
@@ -61,6 +64,7 @@ struct StepArgs {
   int32_t step;       // this step's index within the launch
   int32_t* tokens_out;  // [n_steps][B] greedy tokens, or null
   u64* cand;          // lm_head tile candidates [tile][B] x (value, id), tagged
+  u64* route_hist;    // routed experts: {expert, weight} [kRouteHistSteps][L][B][top_k], or null
 };
 
 // Thread index behind an empty asm: index math derived from it stays inside
@@ -1111,6 +1115,33 @@ DEV void body_merge(Ctx& c, const OpDesc& op) {
   merge_slice(c, op.in, op.out, c.t.a0, c.t.a1, c.t.a2, c.t.a3, (op.pad & 2) != 0);
 }
 
+// ---------------------------------------------------------------- KV append
+// One wavefront writes a new bf16 cache row (D values staged in LDS by the
+// same wavefront) as D/2 packed 32-bit words with agent-scope stores, then
+// waits until every store of the wavefront has completed.
+//
+// Why: in a multi-step launch the chunk bounds follow len = p + 1, so a row
+// appended at step s is read at a later step of the same launch by another
+// chunk task, which may run on another XCD.  XCD L2 caches are not coherent
+// and write back plain stores only at the end of the kernel, so a plain store
+// could stay invisible to that reader.  An agent-scope store writes through to
+// memory, and the wait makes the row globally visible before the task's
+// trigger (issued after the barrier that ends the prologue).  Every later
+// reader of the row orders its loads after that trigger through the event
+// graph: its worker finished an lm_head tile of the writing step, and every
+// lm_head tile depends transitively on every attention chunk of the step.
+// The reader's own L2 cannot hold a stale copy of the row: no task reads a
+// row before the step that appends it.
+template <int D>
+DEV void kv_append(const uint16_t* row, uint16_t* dst, int lane, bool ok) {
+  // the wavefront's own LDS writes above complete before the reads below
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  if (ok && lane < D / 2)
+    __hip_atomic_store(gp((u32*)dst) + lane, ((const u32*)row)[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 // ---------------------------------------------------------------- attention
 // One (sequence b, kv head group gi, chunk ch) task over cache rows
 // [t0, t1) of positions 0..p (p = this step's position of sequence b):
@@ -1135,7 +1166,10 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
   constexpr int VL = D / 2, VR = 64 / VL, VP = NWAVE * VR;  // values
   constexpr int RK = 4, RV = 16;                            // ring depths (passes)
   int pos = c.pos[b];
-  if (pos < 0 || pos >= cap) {
+  // a position outside the cache is reported; the step still runs on a
+  // clamped position so that every wait ends, but appends nothing
+  bool pos_ok = pos >= 0 && pos < cap;
+  if (!pos_ok) {
     if (tid == 0) {
       u32 z = 0;
       __hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_BAD_INPUT, __ATOMIC_RELAXED,
@@ -1148,21 +1182,86 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
   const bool last = ch == C - 1;
   const int T = t1 - t0;
   const int Told = last ? T - 1 : T;  // rows read from the cache (the newest comes from LDS)
-  const size_t base = ((((size_t)op.layer * G.B + b) * Hkv + gi) * (size_t)cap) * D;
-  uint16_t* Kc = a.kv_k + base;
-  uint16_t* Vc = a.kv_v + base;
-  const u32 span = (u32)(Told > 0 ? Told : 0) * (u32)D * 2u;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kc + (size_t)t0 * D), 0, (int)span, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vc + (size_t)t0 * D), 0, (int)span, 0x00020000);
+
+  constexpr int SMAX = kScoreFloats / NG;
+  float* qs = (float*)c.lds;                  // [NG][D], pre-scaled by 1/sqrt(D)
+  uint16_t* knew = (uint16_t*)(qs + NG * D);  // [D] new key (bf16 bits)
+  uint16_t* vnew = knew + D;                  // [D] new value
+  float* sc = (float*)(vnew + D);             // [NG][SMAX] raw scores
+  float* pt = sc + kScoreFloats;              // [row][NG] softmax numerators e^{s - m}
+  float* red = pt + kScoreFloats;             // [NWAVE][NG][D] per-wavefront outputs
+  float* ml = red + NWAVE * NG * D;           // [NG][2] m, l
+  int* pgl = (int*)(ml + 2 * NG);             // paged: physical pages of the chunk's rows
+
+  // Cache rows.  Contiguous: the buffer resource starts at row t0 of (layer,
+  // b, gi).  Paged (the serving layout of paged attention): row t of sequence
+  // b lives at row t mod page of physical page table[b][t / page], the pools
+  // being [L][n_pages][Hkv][page][D]; the resource spans the layer's pool and
+  // the chunk's page numbers are staged in LDS (read again by every ring
+  // refill).  A page number outside the pool is reported and read as page 0.
+  const bool paged = a.page_shift >= 0;
+  const int sh = paged ? a.page_shift : 0, pmask = (1 << sh) - 1;
+  uint16_t* Kc;
+  uint16_t* Vc;
+  u32 span;
+  int lp0 = 0;
+  size_t new_row = (size_t)pos;  // element row of the appended entry (relative to Kc / Vc)
+  if (!paged) {
+    const size_t base = ((((size_t)op.layer * G.B + b) * Hkv + gi) * (size_t)cap) * D;
+    Kc = a.kv_k + base;
+    Vc = a.kv_v + base;
+    span = (u32)(Told > 0 ? Told : 0) * (u32)D * 2u;
+  } else {
+    const size_t pool = (size_t)op.layer * (size_t)a.n_pages * Hkv * ((size_t)1 << sh) * D;
+    Kc = a.kv_k + pool;
+    Vc = a.kv_v + pool;
+    span = (u32)a.n_pages * (u32)Hkv * ((u32)1 << sh) * (u32)D * 2u;
+    const int32_t* tbl = a.page_table + (size_t)b * (cap >> sh);
+    lp0 = t0 >> sh;
+    const int np = Told > 0 ? ((t0 + Told - 1) >> sh) - lp0 + 1 : 0;
+    for (int i = tid; i < np; i += NT) {
+      int ph = tbl[lp0 + i];
+      if (ph < 0 || ph >= a.n_pages) {
+        u32 z = 0;
+        __hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_BAD_INPUT, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ph = 0;
+      }
+      pgl[i] = ph;
+    }
+    if (last) {
+      const int ph = tbl[pos >> sh];
+      if (ph < 0 || ph >= a.n_pages) {
+        pos_ok = false;  // nothing is appended; the error is reported below
+        if (tid == 0) {
+          u32 z = 0;
+          __hip_atomic_compare_exchange_strong(a.status + ST_ERROR, &z, (u32)ERR_BAD_INPUT, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        new_row = ((size_t)(ph * Hkv + gi) << sh) + (size_t)(pos & pmask);
+      }
+    }
+    __syncthreads();
+  }
+  // element offset of cache row t (t0 <= t < t0 + Told) within the resource
+  auto row_off = [&](int t) -> u32 {
+    if (!paged) return (u32)(t - t0) * (u32)D;
+    return ((u32)((pgl[(t >> sh) - lp0] * Hkv + gi) << sh) + (u32)(t & pmask)) * (u32)D;
+  };
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? Kc : Kc + (size_t)t0 * D), 0, (int)span, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? Vc : Vc + (size_t)t0 * D), 0, (int)span, 0x00020000);
   const int krow = wave * KR + lane / KL, kc = lane % KL;  // key row within a pass, 16-byte column
   const int vrow = wave * VR + lane / VL, vc = lane % VL;  // value row within a pass, 4-byte column
   auto koff = [&](int p) -> u32 {
     const int r = p * KP + krow;
-    return r < Told ? (u32)(r * D + kc * 8) * 2u : OOB;
+    return r < Told ? (row_off(t0 + r) + (u32)(kc * 8)) * 2u : OOB;
   };
   auto voff = [&](int p) -> u32 {
     const int r = p * VP + vrow;
-    return r < Told ? (u32)(r * D + vc * 2) * 2u : OOB;
+    return r < Told ? (row_off(t0 + r) + (u32)(vc * 2)) * 2u : OOB;
   };
   const int nk = (T + KP - 1) / KP, nv = (T + VP - 1) / VP;
   u32x4 kr[RK];
@@ -1186,15 +1285,6 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
 
   wait_dep(c);
 
-  constexpr int SMAX = kScoreFloats / NG;
-  float* qs = (float*)c.lds;                  // [NG][D], pre-scaled by 1/sqrt(D)
-  uint16_t* knew = (uint16_t*)(qs + NG * D);  // [D] new key (bf16 bits)
-  uint16_t* vnew = knew + D;                  // [D] new value
-  float* sc = (float*)(vnew + D);             // [NG][SMAX] raw scores
-  float* pt = sc + kScoreFloats;              // [row][NG] softmax numerators e^{s - m}
-  float* red = pt + kScoreFloats;             // [NWAVE][NG][D] per-wavefront outputs
-  float* ml = red + NWAVE * NG * D;           // [NG][2] m, l
-
   // q / k / v prologue: wavefront h handles head h (then k at NG, v at NG+1)
   const u64* qkv = op.in + (size_t)b * G.qkv_stride + (size_t)gi * (NG + 2) * D;
   for (int h = wave; h < NG + 2; h += NWAVE) {
@@ -1210,12 +1300,10 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
     }
     if (h == NG + 1) {
       if (lane < half) {
-        const uint16_t v0 = f2bf(x0), v1 = f2bf(x1);
-        Vc[(size_t)pos * D + lane] = v0;
-        Vc[(size_t)pos * D + lane + half] = v1;
-        vnew[lane] = v0;
-        vnew[lane + half] = v1;
+        vnew[lane] = f2bf(x0);
+        vnew[lane + half] = f2bf(x1);
       }
+      kv_append<D>(vnew, Vc + new_row * D, lane, pos_ok);
       continue;
     }
     const float ss = wave_sum(x0 * x0 + x1 * x1);
@@ -1234,13 +1322,11 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
         qs[h * D + lane] = y0 * G.attn_scale;
         qs[h * D + lane + half] = y1 * G.attn_scale;
       } else {
-        const uint16_t k0 = f2bf(y0), k1 = f2bf(y1);
-        Kc[(size_t)pos * D + lane] = k0;
-        Kc[(size_t)pos * D + lane + half] = k1;
-        knew[lane] = k0;
-        knew[lane + half] = k1;
+        knew[lane] = f2bf(y0);
+        knew[lane + half] = f2bf(y1);
       }
     }
+    if (h == NG) kv_append<D>(knew, Kc + new_row * D, lane, pos_ok);
   }
   __syncthreads();
 
@@ -1366,8 +1452,12 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
     __syncthreads();
     if (tid == 0) {
       u32* arr = (u32*)op.aux + ((size_t)b * Hkv + gi) * kCounterStride;
+      // the counter grows by C per step and a step's chunks all arrive before
+      // the next step's (its O projection waits on every chunk), so the C-th
+      // arrival of a step is the one that completes a multiple of C; this
+      // holds for replayed graphs too, whose recorded epoch never advances
       const u32 old = __hip_atomic_fetch_add(gp(arr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      c.flags[4] = old + 1u == (u32)C * (a.epoch + 1u) ? 1 : 0;
+      c.flags[4] = (old + 1u) % (u32)C == 0u ? 1 : 0;
     }
     __syncthreads();
     if (c.flags[4]) merge_slice(c, op.out, (u64*)op.aux2, b, gi, 0, NG * D);
@@ -1395,6 +1485,7 @@ DEV void route_wave(const StepArgs& a, const OpDesc& op, int lane) {
   const Geom& G = *a.geom;
   const int B = G.B, E = G.E, K = G.topk;
   __shared__ int s_e[16 * 8];
+  __shared__ float s_w[16 * 8];
   u64* route = op.out;
   for (int b = 0; b < B; ++b) {
     const u64* lg = op.in + (size_t)b * E;
@@ -1451,6 +1542,7 @@ DEV void route_wave(const StepArgs& a, const OpDesc& op, int lane) {
     }
     if (lane < K) {
       s_e[b * K + lane] = ej;
+      s_w[b * K + lane] = wj / tot;
       st_t(route + (size_t)(b * K + lane) * 2, (float)ej, a.tag);
       st_t(route + (size_t)(b * K + lane) * 2 + 1, wj / tot, a.tag);
     }
@@ -1459,6 +1551,13 @@ DEV void route_wave(const StepArgs& a, const OpDesc& op, int lane) {
   // (no hardware barrier: in a launch-per-task workgroup only wave 0 is here)
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   __builtin_amdgcn_wave_barrier();
+  // the choice of this step for the host (mk_read_routing), B*K <= 64 records
+  if (a.route_hist && lane < B * K) {
+    const int rec = (((a.step & (kRouteHistSteps - 1)) * G.L + op.layer) * (B * K) + lane) * 2;
+    g_u32* h = (g_u32*)a.route_hist;
+    h[rec] = (u32)s_e[lane];
+    h[rec + 1] = __float_as_uint(s_w[lane]);
+  }
   u64* table = route + route_tb(G);
   u64* act = route + route_ta(G);
   int base = 0;

@@ -893,7 +893,6 @@ void layout(Graph& g) {
         break;
     }
   }
-  (void)L;
   g.off_invfreq = take((int64_t)(D / 2) * 8);
   g.off_geom = take(sizeof(Geom));
   g.off_ops = take((int64_t)g.ops.size() * sizeof(OpDesc));
@@ -921,6 +920,10 @@ void layout(Graph& g) {
   }
   g.off_cand = sc;  // greedy candidates of the lm_head tiles: [tile][B] x (value, id) tagged words
   sc = align_up(sc + (int64_t)std::max(1, g.lm_tiles) * g.B * 2 * 8, 256);
+  if (s.n_experts > 0) {
+    g.off_route_hist = sc;  // {expert, weight} [kRouteHistSteps][L][B][top_k]
+    sc = align_up(sc + (int64_t)kRouteHistSteps * L * g.B * s.top_k * 8, 256);
+  }
   g.scratch_bytes = sc;
   g.trace_bytes = g.opts.trace ? (int64_t)g.tasks.size() * (int64_t)sizeof(mk_trace_rec) : 0;
 }

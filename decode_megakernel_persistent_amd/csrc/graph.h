@@ -79,6 +79,7 @@ struct Graph {
   int64_t arena_bytes = 0, scratch_bytes = 0, trace_bytes = 0;
   int64_t off_geom = 0, off_ops = 0, off_tasks = 0, off_events = 0, off_wloff = 0, off_wlids = 0, off_invfreq = 0;
   int64_t off_counters = 0, off_status = 0, off_progress = 0, off_arrive = 0, off_state_end = 0, off_cand = 0;
+  int64_t off_route_hist = -1;  // routed experts: expert choice history (kRouteHistSteps steps), else -1
   int64_t weight_bytes_step = 0;
 };
 
@@ -130,4 +131,6 @@ struct mk_graph {
   uint32_t persistent_steps = 0;  // of those, steps run by persistent launches (worker arrival/done counts)
   uint32_t tag = 1;    // data tag of the next step
   uint64_t budget_ticks = 0;
+  int32_t last_steps = 0;   // steps of the last launch (mk_read_routing)
+  uint32_t last_tag0 = 0;   // data tag of that launch's first step
 };

@@ -209,8 +209,9 @@ __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
 // The dispatch wavefront: runs the dispatcher's own task list (work-list
 // routing of routed-expert layers), then watches the workers until every one
 // has finished the step, raising the abort flag if that takes longer than the
-// watchdog budget.
-__global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
+// watchdog budget.  Bounded to 64 VGPRs (8 waves per SIMD): two worker
+// wavefronts of up to 224 registers and this one must share a SIMD's 512.
+__global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) {
   const int W = a.n_workers;
   // launch-per-task steps advance the epoch but not the workers' arrival and
   // completion counts, so the targets count persistent steps only
@@ -285,7 +286,7 @@ __global__ void __launch_bounds__(64) mk_dispatch(StepArgs a) {
   }
 }
 #else
-__global__ void __launch_bounds__(64) mk_dispatch(StepArgs a);
+__global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a);
 #endif
 
 #if defined(MK_UNIT_NB)
@@ -429,6 +430,11 @@ StepArgs step_args(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positi
   a.positions = d_positions;
   a.kv_k = (uint16_t*)kv->k;
   a.kv_v = (uint16_t*)kv->v;
+  a.page_table = kv->page_table;
+  a.page_shift = -1;
+  for (int s = 0; kv->page_size > 0 && s < 31; ++s)
+    if ((1 << s) == kv->page_size) a.page_shift = s;
+  a.n_pages = kv->n_pages;
   a.logits = d_logits;
   a.trace = (mk_trace_rec*)g->trace;
   a.budget = g->budget_ticks;
@@ -442,7 +448,41 @@ StepArgs step_args(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positi
   a.step = 0;
   a.tokens_out = d_tokens_out;
   a.cand = (u64*)(scratch + G.off_cand);
+  a.route_hist = G.off_route_hist >= 0 ? (u64*)(scratch + G.off_route_hist) : nullptr;
   return a;
+}
+
+// Checks of a caller's cache description against the graph (see mk_kv_cache).
+bool kv_ok(const Graph& G, const mk_kv_cache* kv, const char* who) {
+  if (!kv || !kv->k || !kv->v) {
+    set_error(std::string(who) + ": null KV cache");
+    return false;
+  }
+  if (kv->capacity != G.cap) {
+    set_error(std::string(who) + ": kv capacity " + std::to_string(kv->capacity) + " differs from the graph's max_ctx " +
+              std::to_string(G.cap));
+    return false;
+  }
+  if (kv->reserved != 0 || kv->page_size < 0) {
+    set_error(std::string(who) + ": bad KV cache description (reserved field or page size)");
+    return false;
+  }
+  if (kv->page_size == 0) return true;
+  const int64_t P = kv->page_size;
+  if (P < 16 || (P & (P - 1)) || G.cap % P) {
+    set_error(std::string(who) + ": page_size must be a power of two >= 16 dividing the capacity");
+    return false;
+  }
+  if (!kv->page_table || kv->n_pages <= 0) {
+    set_error(std::string(who) + ": paged KV cache needs a page table and n_pages > 0");
+    return false;
+  }
+  const int64_t pool = (int64_t)kv->n_pages * G.shape.n_kv_heads * P * G.shape.head_dim * 2;
+  if (pool >= (1LL << 32)) {
+    set_error(std::string(who) + ": one layer's KV pool must stay below 4 GiB");
+    return false;
+  }
+  return true;
 }
 
 // The launch-per-task sequence of one step on `stream`: one mk_lpt launch per
@@ -769,7 +809,7 @@ mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d
     set_error("mk_decode_step: weights not loaded");
     return MK_ERR_STATE;
   }
-  if (!d_tokens || !d_positions || !kv || !kv->k || !kv->v || !d_logits) {
+  if (!d_tokens || !d_positions || !kv || !d_logits) {
     set_error("mk_decode_step: null argument");
     return MK_ERR_ARG;
   }
@@ -788,11 +828,7 @@ mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d
   }
   // tags of this launch stay nonzero and below kGraphTag (reserved for graph replays)
   if (g->tag > kGraphTag - 1u - (uint32_t)n_steps) g->tag = 1;
-  if (kv->capacity != G.cap) {
-    set_error("mk_decode_step: kv capacity " + std::to_string(kv->capacity) + " differs from the graph's max_ctx " +
-              std::to_string(G.cap));
-    return MK_ERR_ARG;
-  }
+  if (!kv_ok(G, kv, "mk_decode_step")) return MK_ERR_ARG;
   hipStream_t stream = (hipStream_t)stream_;
   StepArgs a = step_args(g, d_tokens, d_positions, kv, d_logits, d_tokens_out, n_steps);
   const int nb = kernel_variant(G);
@@ -828,6 +864,8 @@ mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d
     const mk_status rc = launch_lpt(g, a, stream);
     if (rc != MK_OK) return rc;
   }
+  g->last_steps = n_steps;
+  g->last_tag0 = a.tag;
   g->epoch += (uint32_t)n_steps;
   if (g->mode == MK_PERSISTENT) g->persistent_steps += (uint32_t)n_steps;
   g->tag += (uint32_t)n_steps;
@@ -851,10 +889,11 @@ mk_status mk_capture_lpt_graph(mk_graph* g, const int32_t* d_tokens, const int32
     set_error("mk_capture_lpt_graph: weights not loaded");
     return MK_ERR_STATE;
   }
-  if (!d_tokens || !d_positions || !kv || !kv->k || !kv->v || !d_logits || kv->capacity != g->G->cap) {
+  if (!d_tokens || !d_positions || !d_logits) {
     set_error("mk_capture_lpt_graph: bad argument");
     return MK_ERR_ARG;
   }
+  if (!kv_ok(*g->G, kv, "mk_capture_lpt_graph")) return MK_ERR_ARG;
   if (g->G->opts.trace) {
     // the ticketed trace clears its counters with a memset, which a captured graph must not hold
     set_error("mk_capture_lpt_graph: build the graph without trace");
@@ -900,6 +939,8 @@ mk_status mk_lpt_graph_launch(mk_lpt_graph* lg, void* stream) {
   HIPCHK(hipGraphLaunch(lg->exec, (hipStream_t)stream));
   // the replayed tasks trigger their events like any launch-per-task step
   lg->g->epoch += 1;
+  lg->g->last_steps = 1;
+  lg->g->last_tag0 = kGraphTag;
   return MK_OK;
 }
 
@@ -1010,6 +1051,70 @@ mk_status mk_read_trace(mk_graph* g, mk_trace_rec* host_buf, int64_t cap, int64_
   int64_t m = std::min<int64_t>({(int64_t)cnt, cap, (int64_t)G.tasks.size()});
   if (m > 0 && host_buf) HIPCHK(hipMemcpy(host_buf, g->trace, (size_t)m * sizeof(mk_trace_rec), hipMemcpyDeviceToHost));
   *n = (int64_t)cnt;
+  return MK_OK;
+}
+
+mk_status mk_read_routing(mk_graph* g, int32_t step, int32_t* experts, float* weights, float* router_logits,
+                          int64_t cap) {
+  if (!g || !g->G || !g->loaded || !experts || !weights) {
+    set_error("mk_read_routing: bad argument");
+    return MK_ERR_ARG;
+  }
+  Graph& G = *g->G;
+  const mk_model_shape& s = G.shape;
+  if (s.n_experts == 0 || G.off_route_hist < 0) {
+    set_error("mk_read_routing: the graph has no routed experts");
+    return MK_ERR_STATE;
+  }
+  const int64_t n = (int64_t)s.n_layers * G.B * s.top_k;
+  if (cap < n || (router_logits && cap < (int64_t)s.n_layers * G.B * s.n_experts)) {
+    set_error("mk_read_routing: buffers smaller than layers x batch x top_k (x experts for router logits)");
+    return MK_ERR_ARG;
+  }
+  if (step < 0 || step >= g->last_steps || step < g->last_steps - kRouteHistSteps) {
+    set_error("mk_read_routing: step " + std::to_string(step) + " is not one of the last " +
+              std::to_string(kRouteHistSteps) + " steps of the last launch (" + std::to_string(g->last_steps) +
+              " steps)");
+    return MK_ERR_ARG;
+  }
+  if (router_logits && step != g->last_steps - 1) {
+    set_error("mk_read_routing: router logits are kept for the last step of the launch only");
+    return MK_ERR_ARG;
+  }
+  const size_t slot = (size_t)(step % kRouteHistSteps);
+  std::vector<u64> rec((size_t)n);
+  HIPCHK(hipMemcpy(rec.data(), (char*)g->scratch + G.off_route_hist + slot * (size_t)n * 8, (size_t)n * 8,
+                   hipMemcpyDeviceToHost));
+  for (int64_t i = 0; i < n; ++i) {
+    experts[i] = (int32_t)(uint32_t)rec[(size_t)i];
+    const uint32_t wb = (uint32_t)(rec[(size_t)i] >> 32);
+    std::memcpy(&weights[i], &wb, 4);
+  }
+  if (router_logits) {
+    // tagged words [B][E] of each layer's router buffer, tagged with the last step's tag
+    const uint32_t want = g->last_tag0 + (uint32_t)step;
+    const int64_t be = (int64_t)G.B * s.n_experts;
+    std::vector<u64> w((size_t)be);
+    for (int32_t l = 0; l < s.n_layers; ++l) {
+      const std::string name = "rlog." + std::to_string(l);
+      const Buffer* buf = nullptr;
+      for (const Buffer& b : G.bufs)
+        if (b.name == name) buf = &b;
+      if (!buf || buf->off < 0 || buf->words != be) {
+        set_error("mk_read_routing: router buffer of layer " + std::to_string(l) + " not found");
+        return MK_ERR_STATE;
+      }
+      HIPCHK(hipMemcpy(w.data(), (char*)g->scratch + buf->off, (size_t)be * 8, hipMemcpyDeviceToHost));
+      for (int64_t i = 0; i < be; ++i) {
+        if ((uint32_t)(w[(size_t)i] >> 32) != want) {
+          set_error("mk_read_routing: router logits of layer " + std::to_string(l) + " are not the last step's");
+          return MK_ERR_STATE;
+        }
+        const uint32_t vb = (uint32_t)w[(size_t)i];
+        std::memcpy(&router_logits[(size_t)l * be + i], &vb, 4);
+      }
+    }
+  }
   return MK_OK;
 }
 

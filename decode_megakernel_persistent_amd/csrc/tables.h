@@ -133,4 +133,10 @@ constexpr int kMaxStepsPerLaunch = 4096;
 // Data tag of captured launch-per-task graphs (never used by other steps).
 constexpr uint32_t kGraphTag = 0xFFFFFFFFu;
 
+// Routed-expert graphs keep the expert choice of the last kRouteHistSteps
+// steps of a launch (slot = step index within the launch mod this), as
+// {int32 expert, float weight} pairs [slot][layer][sequence][top_k], for
+// mk_read_routing.
+constexpr int kRouteHistSteps = 64;  // a power of two
+
 }  // namespace mk

@@ -120,13 +120,29 @@ typedef struct {
   int32_t on_device;
 } mk_tensor;
 
-/* Contiguous bf16 KV cache, each of k and v laid out [L][B][Hkv][capacity][D].
+/* The caller's bf16 KV cache (device memory), in one of two layouts:
+ *  - contiguous (page_size = 0): k and v each [L][B][Hkv][capacity][D];
+ *  - paged (page_size > 0), the layout of paged attention that a serving
+ *    pipeline keeps inside the megakernel (review page of arXiv 2512.22219,
+ *    adoption paragraph: continuous batching and paged attention run inside
+ *    the mega-kernel): k and v are pools [L][n_pages][Hkv][page_size][D];
+ *    page_table [B][capacity / page_size] (device int32) gives the physical
+ *    page of every logical page of a sequence, so position t of sequence b
+ *    is row t % page_size of page page_table[b][t / page_size].  page_size is
+ *    a power of two, at least 16, dividing capacity; one layer's pool must
+ *    stay below 4 GiB.  A page number outside 0..n_pages-1 met by a step is
+ *    reported by mk_check (MK_ERR_ARG); nothing is written through it.
  * positions[b] of a step is the slot that step writes; attention covers slots
- * 0..positions[b] of sequence b.  capacity must equal the graph's max_ctx. */
+ * 0..positions[b] of sequence b.  capacity must equal the graph's max_ctx.
+ * The library reads the struct at each call (mk_capture_lpt_graph: once). */
 typedef struct {
   void* k;
   void* v;
   int32_t capacity;
+  int32_t page_size;          /* 0 = contiguous */
+  const int32_t* page_table;  /* paged: [B][capacity / page_size], device memory */
+  int32_t n_pages;            /* paged: pages in each of the k and v pools */
+  int32_t reserved;           /* must be zero */
 } mk_kv_cache;
 
 /* One record per executed task (trace mode).  Tickets come from one global
@@ -247,6 +263,19 @@ mk_status mk_read_trace(mk_graph* g, mk_trace_rec* host_buf, int64_t cap, int64_
  * MK_OK or MK_ERR_TRACE (first violation in the message). */
 mk_status mk_check_trace(const mk_graph* g, const mk_trace_rec* recs, int64_t n, uint32_t step,
                          const uint32_t* counters);
+
+/* After sync: the expert choice of step `step` (0-based, within the last
+ * launch; one of its last 64 steps) of a routed-expert graph, as recorded by
+ * the routing task: experts[L][B][top_k] (int32) and their weights (float,
+ * softmax over all experts renormalised over the chosen ones), in the order
+ * chosen.  router_logits (nullable; only for the last step of the launch)
+ * receives the router logits [L][B][n_experts] the choice was made from.
+ * This is the just-in-time, data-dependent part of the step (review page of
+ * arXiv 2512.22219, attack 3: routing needs its own balancing), exposed so
+ * that a caller can check a choice made in fp32 near a tie.  cap: elements
+ * of each buffer.  Errors: MK_ERR_STATE (no routed experts), MK_ERR_ARG. */
+mk_status mk_read_routing(mk_graph* g, int32_t step, int32_t* experts, float* weights, float* router_logits,
+                          int64_t cap);
 
 /* After sync: host copy of the per-event counter totals (events entries). */
 mk_status mk_read_counters(mk_graph* g, uint32_t* host_counters, int64_t cap);

@@ -79,6 +79,13 @@ def _load():
     lib.orc_last_routing.restype = ctypes.c_int32
     lib.orc_last_routing_gap.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     lib.orc_last_routing_gap.restype = ctypes.c_double
+    lib.orc_route_weights.argtypes = [_dp, ctypes.c_int32, ctypes.c_int32, _i32p, _dp]
+    lib.orc_route_gap.argtypes = [_dp, ctypes.c_int32, ctypes.c_int32, _i32p]
+    lib.orc_route_gap.restype = ctypes.c_double
+    lib.orc_last_router_logits.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _dp]
+    lib.orc_last_router_logits.restype = ctypes.c_int32
+    lib.orc_force_routing.argtypes = [ctypes.c_void_p, _i32p]
+    lib.orc_force_routing.restype = ctypes.c_int32
     _lib = lib
     return lib
 
@@ -136,6 +143,22 @@ def route(logits, k: int) -> Tuple[np.ndarray, np.ndarray]:
     w = np.empty(k, dtype=np.float64)
     _load().orc_route(_d(lg), lg.size, k, e.ctypes.data_as(_i32p), _d(w))
     return e, w
+
+
+def route_weights(logits, experts) -> np.ndarray:
+    """Weights of a given expert choice: softmax over all logits, renormalised over the choice."""
+    lg = _f64(logits)
+    e = np.ascontiguousarray(experts, dtype=np.int32)
+    w = np.empty(e.size, dtype=np.float64)
+    _load().orc_route_weights(_d(lg), lg.size, e.size, e.ctypes.data_as(_i32p), _d(w))
+    return w
+
+
+def route_gap(logits, experts) -> float:
+    """Smallest chosen logit minus the largest unchosen one (0 at an exact tie)."""
+    lg = _f64(logits)
+    e = np.ascontiguousarray(experts, dtype=np.int32)
+    return float(_load().orc_route_gap(_d(lg), lg.size, e.size, e.ctypes.data_as(_i32p)))
 
 
 # ----------------------------------------------------------------- model
@@ -213,6 +236,26 @@ class Oracle:
         """Smallest router-logit gap between a chosen and an unchosen expert of
         sequence b over the layers of the last decode (inf for dense models)."""
         return float(_load().orc_last_routing_gap(self._h, b))
+
+    def last_router_logits(self, layer: int, b: int) -> np.ndarray:
+        """Router logits [E] of (layer, sequence b) in the last decode step."""
+        out = np.empty(self.shape.n_experts, dtype=np.float64)
+        if _load().orc_last_router_logits(self._h, layer, b, _d(out)):
+            raise RuntimeError("no router logits (dense model or bad index)")
+        return out
+
+    def force_routing(self, experts: Optional[np.ndarray]):
+        """Evaluate the following decode steps on a given expert choice
+        [L][B][top_k] (None: the oracle's own top-k)."""
+        if experts is None:
+            rc = _load().orc_force_routing(self._h, None)
+        else:
+            e = np.ascontiguousarray(experts, dtype=np.int32)
+            s = self.shape
+            assert e.shape == (s.n_layers, self.batch, s.top_k), e.shape
+            rc = _load().orc_force_routing(self._h, e.ctypes.data_as(_i32p))
+        if rc:
+            raise RuntimeError(_load().orc_last_error().decode())
 
     def last_routing(self, layer: int, b: int) -> Tuple[np.ndarray, np.ndarray]:
         k = self.shape.top_k

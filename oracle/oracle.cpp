@@ -238,6 +238,36 @@ void orc_route(const double* logits, int32_t E, int32_t k, int32_t* experts, dou
   for (int j = 0; j < k; ++j) weights[j] /= tot;
 }
 
+// Weights of a given choice of k experts: the softmax over all E router
+// logits, renormalised over the chosen experts (the same definition as
+// orc_route, with the choice taken as input instead of the k largest).
+void orc_route_weights(const double* logits, int32_t E, int32_t k, const int32_t* experts, double* weights) {
+  double m = -INFINITY;
+  for (int e = 0; e < E; ++e) m = std::max(m, logits[e]);
+  double den = 0.0;
+  for (int e = 0; e < E; ++e) den += std::exp(logits[e] - m);
+  double tot = 0.0;
+  for (int j = 0; j < k; ++j) {
+    weights[j] = std::exp(logits[experts[j]] - m) / den;
+    tot += weights[j];
+  }
+  for (int j = 0; j < k; ++j) weights[j] /= tot;
+}
+
+// How close a top-k choice came to a tie: the smallest logit among the k
+// chosen experts minus the largest logit among the others (0 for an exact
+// tie across the boundary; +inf when k = E).
+double orc_route_gap(const double* logits, int32_t E, int32_t k, const int32_t* experts) {
+  std::vector<char> chosen((size_t)E, 0);
+  for (int j = 0; j < k; ++j) chosen[experts[j]] = 1;
+  double lo_in = INFINITY, hi_out = -INFINITY;
+  for (int e = 0; e < E; ++e) {
+    if (chosen[e]) lo_in = std::min(lo_in, logits[e]);
+    else hi_out = std::max(hi_out, logits[e]);
+  }
+  return lo_in - hi_out;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- the model
@@ -252,6 +282,9 @@ struct orc_model {
   std::vector<int32_t> route_e;
   std::vector<double> route_w;
   std::vector<double> route_gap;  // [L][B]: smallest chosen logit minus largest unchosen logit
+  std::vector<double> route_logits;  // [L][B][E]: router logits of the last decode step
+  // optional forced expert choice [L][B][top_k] for the next decode steps
+  std::vector<int32_t> forced;
 };
 
 namespace {
@@ -364,22 +397,22 @@ void ffn_block(orc_model* m, int l, int b, double* x) {
   matvec_par(m, need(m, pre + "router", E, H), h.data(), E, H, r.data());
   std::vector<int32_t> ex((size_t)Kt);
   std::vector<double> wt((size_t)Kt);
-  orc_route(r.data(), E, Kt, ex.data(), wt.data());
+  if (b >= 0 && !m->forced.empty()) {
+    // a given choice (another decoder's valid routing), weighted by the definition
+    for (int j = 0; j < Kt; ++j) ex[j] = m->forced[((size_t)l * m->B + b) * Kt + j];
+    orc_route_weights(r.data(), E, Kt, ex.data(), wt.data());
+  } else {
+    orc_route(r.data(), E, Kt, ex.data(), wt.data());
+  }
   if (b >= 0) {
     for (int j = 0; j < Kt; ++j) {
       m->route_e[((size_t)l * m->B + b) * Kt + j] = ex[j];
       m->route_w[((size_t)l * m->B + b) * Kt + j] = wt[j];
     }
+    std::copy(r.begin(), r.end(), m->route_logits.begin() + ((size_t)l * m->B + b) * E);
     // how close the top-k choice came to a tie (in logit units): a decision
     // another precision may take differently when this is tiny
-    double lo_in = INFINITY, hi_out = -INFINITY;
-    std::vector<char> chosen((size_t)E, 0);
-    for (int j = 0; j < Kt; ++j) chosen[ex[j]] = 1;
-    for (int e = 0; e < E; ++e) {
-      if (chosen[e]) lo_in = std::min(lo_in, r[e]);
-      else hi_out = std::max(hi_out, r[e]);
-    }
-    m->route_gap[(size_t)l * m->B + b] = lo_in - hi_out;
+    m->route_gap[(size_t)l * m->B + b] = orc_route_gap(r.data(), E, Kt, ex.data());
   }
   std::vector<double> acc((size_t)H, 0.0);
   for (int j = 0; j < Kt; ++j) {
@@ -427,6 +460,7 @@ orc_model* orc_create(const orc_shape* s, int32_t batch, int32_t cap, int32_t nt
       m->route_e.assign((size_t)s->n_layers * batch * s->top_k, -1);
       m->route_w.assign((size_t)s->n_layers * batch * s->top_k, 0.0);
       m->route_gap.assign((size_t)s->n_layers * batch, INFINITY);
+      m->route_logits.assign((size_t)s->n_layers * batch * s->n_experts, 0.0);
     }
     return m;
   } catch (const std::exception& e) {
@@ -539,6 +573,47 @@ double orc_last_routing_gap(const orc_model* m, int32_t b) {
   if (!m || m->s.n_experts == 0) return g;
   for (int l = 0; l < m->s.n_layers; ++l) g = std::min(g, m->route_gap[(size_t)l * m->B + b]);
   return g;
+}
+
+// Router logits of (layer, b) in the last orc_decode: E values.
+int32_t orc_last_router_logits(const orc_model* m, int32_t layer, int32_t b, double* out) {
+  if (!m || m->s.n_experts == 0 || layer < 0 || layer >= m->s.n_layers || b < 0 || b >= m->B) return -1;
+  const int E = m->s.n_experts;
+  std::copy(m->route_logits.begin() + ((size_t)layer * m->B + b) * E,
+            m->route_logits.begin() + ((size_t)layer * m->B + b + 1) * E, out);
+  return 0;
+}
+
+// Force the expert choice of the following orc_decode calls: experts
+// [L][B][top_k] (each row k distinct ids), weighted by orc_route_weights; NULL
+// restores the top-k choice.  The full causal recompute is never forced.
+int32_t orc_force_routing(orc_model* m, const int32_t* experts) {
+  if (!m || m->s.n_experts == 0) {
+    g_err = "no routed experts";
+    return -1;
+  }
+  if (!experts) {
+    m->forced.clear();
+    return 0;
+  }
+  const int E = m->s.n_experts, Kt = m->s.top_k;
+  const size_t n = (size_t)m->s.n_layers * m->B * Kt;
+  for (size_t i = 0; i < n; i += Kt) {
+    for (int j = 0; j < Kt; ++j) {
+      const int e = experts[i + j];
+      if (e < 0 || e >= E) {
+        g_err = "forced expert id out of range";
+        return -1;
+      }
+      for (int u = 0; u < j; ++u)
+        if (experts[i + u] == e) {
+          g_err = "forced experts of one (layer, sequence) must be distinct";
+          return -1;
+        }
+    }
+  }
+  m->forced.assign(experts, experts + n);
+  return 0;
 }
 
 // Routing chosen by the last orc_decode for (layer, b): top_k experts and weights.

@@ -1,8 +1,9 @@
 """Launch-per-task mode captured into a HIP graph (mk_capture_lpt_graph).
 
 Every replay must equal, bit for bit, an eager launch-per-task step of the
-same kernels on the same inputs; replays alternate with the program's own
-eager work and synchronisations, and each one is checked.  A persistent step
+same kernels on the same inputs, and match the oracle (logits relative L2 <=
+1e-2, tokens where the top-2 margin exceeds 0.05); replays alternate with the
+program's own eager work and synchronisations, and each one is checked.  A persistent step
 after the replays must still match (the replays count as steps for the event
 epochs), and the KV caches must agree at the end.
 """
@@ -25,12 +26,19 @@ def new_session(w, prep, **kw):
     return sess
 
 
-@pytest.mark.parametrize("wname,per_task", [("tiny", 0), ("tiny", 1), ("qwen3-0.6b", 0)])
-def test_lpt_graph_replays_match_eager_steps(wname, per_task):
+@pytest.mark.parametrize("wname,per_task,merge_tasks", [("tiny", 0, 0), ("tiny", 1, 0), ("tiny", 0, 2),
+                                                        ("qwen3-0.6b", 0, 0), ("qwen3-0.6b", 0, 2)])
+def test_lpt_graph_replays_match_eager_steps(wname, per_task, merge_tasks):
+    # merge_tasks = 2: the last-arriving attention chunk merges, found from an
+    # arrival counter that every replay advances
     w = synth.WORKLOADS[wname]
     prep = harness.prepare(w)
-    gs = new_session(w, prep)
-    es = new_session(w, prep)
+    gs = new_session(w, prep, merge_tasks=merge_tasks)
+    es = new_session(w, prep, merge_tasks=merge_tasks)
+    orc = harness.oracle.Oracle(w.shape, w.batch, w.capacity)
+    orc.set_weights(prep.weights)
+    orc.K[...] = prep.k0
+    orc.V[...] = prep.v0
     try:
         gs.set_mode(mk.MK_LAUNCH_PER_TASK, per_task)
         es.set_mode(mk.MK_LAUNCH_PER_TASK, per_task)
@@ -51,7 +59,12 @@ def test_lpt_graph_replays_match_eager_steps(wname, per_task):
             lg_e = lg_e.cpu().numpy()
             assert float(torch.ones(1 << 16, device=gs.device).sum().item()) == float(1 << 16)
             np.testing.assert_array_equal(lg_g, lg_e)
-            tok, pos = harness.oracle.greedy(lg_e), pos + 1
+            # and the replay against the oracle (teacher forcing with its tokens)
+            lg_o = orc.decode(tok, pos)
+            rep = harness.compare(lg_g, lg_o)
+            harness.log(f"[graph] replay {s}: rel_l2 {max(r['rel_l2'] for r in rep):.2e}")
+            assert all(r["ok"] for r in rep), rep
+            tok, pos = harness.oracle.greedy(lg_o), pos + 1
         # a persistent step after the replays
         gs.set_mode(mk.MK_PERSISTENT)
         es.set_mode(mk.MK_PERSISTENT)

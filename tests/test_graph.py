@@ -251,3 +251,79 @@ def test_lm_head_terminal_event(wname, gemv):
         assert sorted(tasks[lm, 4].tolist()) == list(range(len(lm)))
     finally:
         mk.mk_destroy_graph(g)
+
+
+def _upstream_tasks(tasks, event):
+    """Every task the given event depends on, transitively (reverse walk over triggers)."""
+    prod = {}
+    for t, e in enumerate(tasks[:, 3]):
+        if e >= 0:
+            prod.setdefault(int(e), []).append(t)
+    seen, stack, evs = set(), [int(event)], set()
+    while stack:
+        e = stack.pop()
+        if e in evs:
+            continue
+        evs.add(e)
+        for t in prod.get(e, []):
+            if t not in seen:
+                seen.add(t)
+                if tasks[t, 2] >= 0:
+                    stack.append(int(tasks[t, 2]))
+    return seen
+
+
+@pytest.mark.parametrize("wname,steps", [("qwen3-0.6b", 32), ("tiny-40", 40)])
+def test_multistep_kv_rows_cross_xcds_only_after_an_ordering_event(wname, steps):
+    # In a launch of n steps, the row appended at step s by the last chunk
+    # task of (layer, sequence, kv head) is read at later steps by whichever
+    # chunk covers it as the positions grow.  List those reads: some are by a
+    # worker on another XCD (worker index mod 8 on gfx950).  The append is an
+    # agent-scope store completed before its task triggers; the reader is
+    # ordered after that trigger because (1) every worker's list of a step
+    # ends with an lm_head tile and (2) the lm_head tiles depend transitively
+    # on every attention chunk of the step, so a worker starts the next step's
+    # tasks only after every append of the step has become visible.
+    import dataclasses
+    w = (dataclasses.replace(synth.WORKLOADS["tiny"], name="tiny-40", steps=40) if wname == "tiny-40"
+         else synth.WORKLOADS[wname])
+    g = mk.mk_build_graph(w.shape, w.batch, w.capacity, mk.make_opts(num_workers=256))
+    try:
+        tasks = mk.mk_get_tasks(g)
+        off, ids = mk.mk_get_worker_lists(g)
+        st = mk.mk_graph_stats(g)
+        C, W = st.attn_chunks, st.workers
+        worker = np.empty(len(tasks), dtype=np.int64)
+        for wk in range(W):
+            worker[ids[off[wk]:off[wk + 1]]] = wk
+        attn = np.nonzero(tasks[:, 0] == mk.OP_KINDS.index("attn"))[0]
+        where = {(int(tasks[t, 1]), int(tasks[t, 4]), int(tasks[t, 5]), int(tasks[t, 6])): int(worker[t]) for t in attn}
+        # the in-launch rows and their readers
+        p0 = int(synth.lengths(w)[0]) if not w.prompt else w.prompt
+        cross = reads = 0
+        for (l, b, gi, ch), wk in where.items():
+            if ch != C - 1:
+                continue
+            for s in range(steps):
+                r = p0 + s                      # row appended at step s
+                for s2 in range(s + 1, steps):
+                    ln = p0 + s2 + 1
+                    c = next(c for c in range(C) if c * ln // C <= r < (c + 1) * ln // C)
+                    if c != C - 1:
+                        reads += 1
+                        if where[(l, b, gi, c)] % 8 != wk % 8:
+                            cross += 1
+        assert cross > 0, "the configuration never moves a row across XCDs: the test would not cover the hazard"
+        # (1) the last task of every worker's list is an lm_head tile
+        lm = mk.OP_KINDS.index("lmhead")
+        for wk in range(W):
+            assert tasks[ids[off[wk + 1] - 1], 0] == lm
+        # (2) the lm_head tiles wait on one event upstream of every attention chunk
+        lm_tasks = np.nonzero(tasks[:, 0] == lm)[0]
+        deps = set(tasks[lm_tasks, 2].tolist())
+        assert len(deps) == 1
+        up = _upstream_tasks(tasks, deps.pop())
+        assert set(attn.tolist()) <= up
+        print(f"{wname}: {reads} in-launch row reads by other chunks, {cross} of them on another XCD")
+    finally:
+        mk.mk_destroy_graph(g)

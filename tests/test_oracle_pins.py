@@ -181,6 +181,46 @@ def test_route_ties_go_to_lower_index():
     np.testing.assert_array_equal(e, [3, 9, 12, 0])
 
 
+def test_route_gap_hand_written():
+    # smallest chosen logit minus largest unchosen logit
+    assert oracle.route_gap([3.0, 1.0, 2.0, 0.0], [0, 2]) == 1.0
+    assert oracle.route_gap([-5.0, -1.0, -3.0, -2.0], [1, 3]) == 1.0
+    assert oracle.route_gap([0.5, 0.25, 4.0], [2]) == 3.5
+    # exact ties across the boundary: gap 0, whichever tied expert is chosen
+    assert oracle.route_gap([1.0, 1.0, 0.0], [0]) == 0.0
+    assert oracle.route_gap([1.0, 1.0, 0.0], [1]) == 0.0
+    # a choice that is not a top-k has a negative gap
+    assert oracle.route_gap([3.0, 1.0, 2.0, 0.0], [0, 1]) == -1.0
+    # every expert chosen: nothing to compare against
+    assert oracle.route_gap([1.0, 2.0], [0, 1]) == math.inf
+
+
+def test_route_weights_closed_form():
+    lg = np.array([0.3, -1.2, 2.0, 0.7])
+    w = oracle.route_weights(lg, [0, 2])
+    ea, ec = math.exp(0.3), math.exp(2.0)
+    np.testing.assert_allclose(w, [ea / (ea + ec), ec / (ea + ec)], rtol=1e-14)
+    # the weights follow the listed order
+    np.testing.assert_allclose(oracle.route_weights(lg, [2, 0]), w[::-1], rtol=1e-15)
+    # one expert carries the whole weight
+    assert oracle.route_weights(lg, [3])[0] == 1.0
+    # the top-k choice gets exactly route()'s weights
+    for trial in range(5):
+        lg = RNG.standard_normal(64) * 2
+        e, want = oracle.route(lg, 6)
+        np.testing.assert_array_equal(oracle.route_weights(lg, e), want)
+
+
+def test_top2_margin_hand_written():
+    # top-1 minus top-2 logit, per row; 0 when the two largest tie
+    assert oracle.top2_margin(np.array([3.0, 1.0, 2.0])) == 1.0
+    assert oracle.top2_margin(np.array([5.0, 5.0, 1.0])) == 0.0
+    assert oracle.top2_margin(np.array([-1.0, -3.0, -2.0])) == 1.0
+    assert oracle.top2_margin(np.array([0.0, -7.5])) == 7.5
+    rows = np.array([[0.0, 0.5, 0.25, 0.125], [2.0, -1.0, 2.0, 1.5], [-4.0, -6.0, -4.5, -9.0]])
+    np.testing.assert_array_equal(oracle.top2_margin(rows), [0.25, 0.0, 0.5])
+
+
 # ----------------------------------------------------------------- whole decoder
 MICRO = synth.ModelShape(n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, intermediate=96,
                          vocab=97, tied_embeddings=False)
@@ -225,6 +265,74 @@ def test_moe_decoder_matches_independent_torch_model():
         lg = o.decode([t], [p])[0]
     ref = torch_ref.forward_last_logits(shape, ws, toks)
     assert np.linalg.norm(lg - ref) <= 1e-6 * np.linalg.norm(ref)
+
+
+MOE_MICRO = synth.ModelShape(n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=1, head_dim=16, intermediate=0,
+                             vocab=61, tied_embeddings=False, n_experts=6, top_k=2, expert_intermediate=32)
+
+
+def _moe_run(forced=None):
+    ws = _micro_weights(MOE_MICRO, seed=3)
+    toks = synth.uniform_i32("pin.tokens3", 7, 5, 0, MOE_MICRO.vocab - 1)
+    o = oracle.Oracle(MOE_MICRO, batch=1, cap=8, threads=1)
+    o.set_weights(ws)
+    for p, t in enumerate(toks[:-1]):
+        o.decode([t], [p])
+    if forced is not None:
+        o.force_routing(np.asarray(forced, dtype=np.int32).reshape(MOE_MICRO.n_layers, 1, MOE_MICRO.top_k))
+    lg = o.decode([toks[-1]], [len(toks) - 1])[0]
+    return o, ws, toks, lg
+
+
+def test_router_logits_and_routing_gap_match_torch():
+    # the recorded router logits of the last step and the smallest routing gap
+    # over the layers, against router logits from the independent torch model
+    o, ws, toks, _ = _moe_run()
+    rl = []
+    torch_ref.forward_last_logits(MOE_MICRO, ws, toks, router_out=rl)
+    gaps = []
+    for l in range(MOE_MICRO.n_layers):
+        np.testing.assert_allclose(o.last_router_logits(l, 0), rl[l], rtol=1e-9, atol=1e-12)
+        r = torch.from_numpy(rl[l])
+        top = torch.topk(r, MOE_MICRO.top_k).indices
+        rest = torch.ones(MOE_MICRO.n_experts, dtype=torch.bool)
+        rest[top] = False
+        gaps.append(float(r[top].min() - r[rest].max()))
+        assert set(o.last_routing(l, 0)[0].tolist()) == set(top.tolist())
+    assert abs(o.last_routing_gap(0) - min(gaps)) < 1e-9
+
+
+def test_forced_routing_matches_torch_with_the_same_choice():
+    # the last step evaluated on a choice that is not the top-k: in every layer
+    # the second chosen expert is replaced by the best unchosen one
+    o, ws, toks, natural = _moe_run()
+    forced = []
+    for l in range(MOE_MICRO.n_layers):
+        e, _ = o.last_routing(l, 0)
+        r = o.last_router_logits(l, 0)
+        order = np.argsort(-r, kind="stable")
+        forced.append([int(e[0]), int(order[MOE_MICRO.top_k])])
+    o2, _, _, lg = _moe_run(forced)
+    ref = torch_ref.forward_last_logits(MOE_MICRO, ws, toks, forced_last=forced)
+    assert np.linalg.norm(lg - ref) <= 1e-6 * np.linalg.norm(ref)
+    assert np.linalg.norm(lg - natural) > 1e-3 * np.linalg.norm(natural)  # the choice mattered
+    for l in range(MOE_MICRO.n_layers):
+        e, w = o2.last_routing(l, 0)
+        assert e.tolist() == forced[l]
+        assert abs(w.sum() - 1.0) < 1e-12
+    # forcing the oracle's own choice changes nothing, bit for bit
+    own = [o.last_routing(l, 0)[0].tolist() for l in range(MOE_MICRO.n_layers)]
+    _, _, _, same = _moe_run(own)
+    np.testing.assert_array_equal(same, natural)
+
+
+def test_forced_routing_rejects_bad_choices():
+    o = oracle.Oracle(MOE_MICRO, batch=1, cap=8, threads=1)
+    with pytest.raises(RuntimeError):
+        o.force_routing(np.array([[[0, 0]], [[1, 2]]], dtype=np.int32))   # repeated expert
+    with pytest.raises(RuntimeError):
+        o.force_routing(np.array([[[0, 6]], [[1, 2]]], dtype=np.int32))   # id out of range
+    o.force_routing(None)
 
 
 def test_moe_with_one_expert_reduces_to_dense_mlp():

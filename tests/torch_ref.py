@@ -34,8 +34,14 @@ def _round_bf16(t: torch.Tensor) -> torch.Tensor:
     return t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
 
 
-def forward_last_logits(shape, ws, tokens) -> np.ndarray:
-    """Logits (float64, [V]) at the last position of `tokens` (positions 0..n-1)."""
+def forward_last_logits(shape, ws, tokens, forced_last=None, router_out=None) -> np.ndarray:
+    """Logits (float64, [V]) at the last position of `tokens` (positions 0..n-1).
+
+    Routed models: ``forced_last[l]`` (optional) is the expert choice of layer l
+    at the last position, weighted by its softmax probabilities renormalised
+    over the choice; earlier positions always take the top-k.  If given,
+    ``router_out`` (a list) receives the router logits [E] of the last position
+    per layer."""
     s = shape
     H, D, Hq, Hkv = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads
     G = Hq // Hkv
@@ -69,8 +75,14 @@ def forward_last_logits(shape, ws, tokens) -> np.ndarray:
             x = x + F.linear(a, _w(ws, p + "w_down").reshape(H, I))
         else:
             Ie, E, K = s.expert_intermediate, s.n_experts, s.top_k
-            probs = torch.softmax(F.linear(h2, _w(ws, p + "router").reshape(E, H)), dim=-1)
+            rl = F.linear(h2, _w(ws, p + "router").reshape(E, H))
+            if router_out is not None:
+                router_out.append(rl[-1].numpy().copy())
+            probs = torch.softmax(rl, dim=-1)
             top_p, top_e = torch.topk(probs, K, dim=-1)
+            if forced_last is not None:
+                top_e[-1] = torch.as_tensor(np.asarray(forced_last[l], dtype=np.int64))
+                top_p[-1] = probs[-1, top_e[-1]]
             top_p = top_p / top_p.sum(dim=-1, keepdim=True)
             y = torch.zeros_like(x)
             for t in range(n):
