@@ -26,16 +26,19 @@ MARGIN = 0.05
 # Routed experts: the expert choice is an integer decided by floating point,
 # in fp32 on the GPU (from its own router logits) and in fp64 in the oracle,
 # so the two may choose differently where two router logits are within
-# rounding of each other.  The GPU's choice is never exempted: the GPU's
-# router logits must match the oracle's (evaluated on the same choice) within
-# ROUTE_TOL, its choice must be an exact top-k of its own router logits, and a
-# valid top-k of the oracle's up to ROUTE_TOL; where it differs from the
-# oracle's own top-k the oracle is re-run on the GPU's choice (the same
-# definition, another valid decision) and the logits are compared with that.
-# ROUTE_TOL bounds the fp32 router-logit error (|r| ~ 1, hidden state within
-# ~1e-5 relative of the oracle's), checked directly on every single-step
-# comparison.
-ROUTE_TOL = 3e-4
+# rounding of each other.  The GPU's choice is never exempted:
+#  - its router logits are logits too: relative L2 error <= REL_L2_TOL against
+#    the oracle's (evaluated on the same choice of the earlier layers);
+#  - its choice must be the exact top-k of its own router logits;
+#  - its choice must be a top-k of the oracle's router logits up to twice the
+#    GPU's measured router-logit error on that row (what two valid decisions
+#    within that error can differ by), or up to ROUTE_GAP_REL of the row's RMS
+#    for steps whose GPU router logits are not kept (earlier steps of a
+#    multi-step launch);
+#  - where it differs from the oracle's own top-k, the oracle is re-run on the
+#    GPU's choice (the same definition, the other valid decision) and the
+#    logits are compared with that.
+ROUTE_GAP_REL = 2e-3
 
 
 @dataclasses.dataclass
@@ -110,11 +113,10 @@ def oracle_reference(orc, tok, pos, routing=None, info: Optional[dict] = None) -
     Dense models: the oracle's decode.  Routed models (``routing`` = the GPU's
     (experts [L,B,K], weights [L,B,K], router logits [L,B,E] or None) for
     this step): the oracle decodes with its own top-k; if the GPU chose a
-    different set anywhere, the GPU's choice is checked to be a top-k of the
-    oracle's router logits up to ROUTE_TOL and the oracle re-decodes the step
-    on it.  In either case the GPU's router logits (when given) must match the
-    oracle's within ROUTE_TOL, the GPU's choice must be the exact top-k of its
-    own router logits, and its weights those of the definition.  The oracle's
+    different set anywhere, the oracle re-decodes the step on the GPU's
+    choice.  The GPU's choice is then checked layer by layer as described
+    above (router logits, exact top-k of its own, top-k of the oracle's within
+    the measured error) and its weights against the definition.  The oracle's
     cache afterwards holds the keys/values of the run returned."""
     lg = orc.decode(tok, pos)
     if orc.shape.n_experts == 0:
@@ -133,33 +135,54 @@ def oracle_reference(orc, tok, pos, routing=None, info: Optional[dict] = None) -
     for l in range(L):
         for b in range(B):
             r_o = orc.last_router_logits(l, b)
-            gap = oracle.route_gap(r_o, e_g[l, b])
-            min_gap = min(min_gap, gap)
-            assert gap >= -ROUTE_TOL, f"layer {l} seq {b}: GPU experts {e_g[l, b]} are not a top-{K} (gap {gap})"
-            np.testing.assert_allclose(w_g[l, b], oracle.route_weights(r_o, e_g[l, b]), rtol=0, atol=1e-4)
+            rms = float(np.sqrt(np.mean(r_o * r_o)))
+            tol = ROUTE_GAP_REL * rms
             if rl_g is not None:
-                err = float(np.abs(rl_g[l, b].astype(np.float64) - r_o).max())
-                assert err <= ROUTE_TOL, f"layer {l} seq {b}: router logits differ by {err}"
-                assert is_topk(rl_g[l, b].astype(np.float64), e_g[l, b], 1e-6), \
+                r_g = rl_g[l, b].astype(np.float64)
+                err = float(np.abs(r_g - r_o).max())
+                rel = float(np.linalg.norm(r_g - r_o) / np.linalg.norm(r_o))
+                assert rel <= REL_L2_TOL, f"layer {l} seq {b}: router logits relative L2 error {rel}"
+                assert is_topk(r_g, e_g[l, b], 1e-6 * rms), \
                     f"layer {l} seq {b}: GPU experts {e_g[l, b]} are not the top-{K} of its router logits"
+                tol = 2.0 * err + 1e-6 * rms
                 if info is not None:
                     info["router_err"] = max(info.get("router_err", 0.0), err)
+                    info["router_rel"] = max(info.get("router_rel", 0.0), rel)
+            gap = oracle.route_gap(r_o, e_g[l, b])
+            min_gap = min(min_gap, gap)
+            assert gap >= -tol, f"layer {l} seq {b}: GPU experts {e_g[l, b]} are not a top-{K} (gap {gap}, tol {tol})"
+            np.testing.assert_allclose(w_g[l, b], oracle.route_weights(r_o, e_g[l, b]), rtol=0, atol=1e-3)
     if info is not None:
         info["routing_diffs"] = info.get("routing_diffs", 0) + len(diff)
         info["min_route_gap"] = min(info.get("min_route_gap", np.inf), min_gap)
     return lg
 
 
-def kv_row_ulps(dev: np.ndarray, orc: np.ndarray) -> float:
-    """Largest difference between bf16 cache rows [..., D], in units of one
-    bf16 ulp at each element's magnitude (floored at a quarter of its row's
-    RMS, so that elements near zero are measured on the row's scale)."""
+def kv_row_errors(dev: np.ndarray, orc: np.ndarray):
+    """Differences between bf16 cache rows [..., D] appended by the GPU and by
+    the oracle: (largest difference in units of one bf16 ulp at each
+    element's magnitude, floored at a quarter of its row's RMS; largest
+    difference beyond that one ulp, relative to the row's RMS; fraction of
+    elements that differ at all)."""
     d = synth.bf16_to_f32(dev.astype(np.uint16)).astype(np.float64)
     o = synth.bf16_to_f32(orc.astype(np.uint16)).astype(np.float64)
-    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True)) + 1e-300
     scale = np.maximum(np.abs(o), rms / 4) + 1e-300
     ulp = np.exp2(np.floor(np.log2(scale)) - 7)  # bf16: 8 significant bits
-    return float((np.abs(d - o) / ulp).max())
+    diff = np.abs(d - o)
+    return (float((diff / ulp).max()), float((np.maximum(diff - ulp, 0.0) / rms).max()),
+            float(np.mean(dev != orc)))
 
 
-KV_ULP_TOL = 1.0
+# Both sides round the same new key/value to bf16 (round to nearest even).
+# Rounding alone makes them differ by at most one ulp where their unrounded
+# values straddle a rounding boundary; the unrounded values differ by the
+# decoder's own fp32 error, for which the stated bound on logits (1e-2
+# relative) is taken: every element must lie within one ulp plus 1e-2 of its
+# row's RMS.  Measured beyond the ulp: 0 on the VALU tiles (batch <= 4) and up
+# to ~1.5e-3 of the RMS on the MFMA tiles (batch 16, bf16 hi/lo inputs: ~3e-5
+# logits error, ~3e-4 for a sequence attending over few positions).  At most
+# a quarter of the elements may differ at all: a wrong rounding mode
+# (truncation) changes about half of them.
+KV_EXCESS_TOL = 1e-2
+KV_MISMATCH_TOL = 0.25
