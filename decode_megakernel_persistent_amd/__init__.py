@@ -128,6 +128,7 @@ def lib():
         "mk_load_weights": [_vp, ctypes.POINTER(mk_tensor), ctypes.c_int32, _vp, _vp, _vp, _vp],
         "mk_decode_step": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, _vp],
         "mk_decode_steps": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, _vp, ctypes.c_int32, _vp],
+        "mk_decode_step_noalloc": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, _vp],
         "mk_capture_lpt_graph": [_vp, _vp, _vp, ctypes.POINTER(mk_kv_cache), _vp, ctypes.POINTER(_vp)],
         "mk_lpt_graph_launch": [_vp, _vp],
         "mk_set_mode": [_vp, ctypes.c_int32, ctypes.c_int32],
@@ -162,6 +163,7 @@ def lib():
 
 
 EXPORTED = ["mk_build_graph", "mk_workspace_size", "mk_load_weights", "mk_decode_step", "mk_decode_steps",
+            "mk_decode_step_noalloc",
             "mk_capture_lpt_graph", "mk_lpt_graph_launch", "mk_lpt_graph_destroy", "mk_set_mode", "mk_check",
             "mk_read_trace", "mk_check_trace", "mk_read_counters", "mk_read_routing", "mk_simulate", "mk_graph_stats", "mk_dump_graph",
             "mk_get_tasks", "mk_get_events", "mk_get_worker_lists", "mk_get_raw_edges", "mk_destroy_graph",
@@ -243,6 +245,12 @@ def mk_load_weights(g: int, tensors: Sequence[Tuple[str, object]], d_arena: int,
 
 def mk_decode_step(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int, stream: int = 0):
     _chk(lib().mk_decode_step(g, d_tokens, d_positions, ctypes.byref(kv), d_logits, stream or None), "mk_decode_step")
+
+
+def mk_decode_step_noalloc(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int,
+                           stream: int = 0):
+    _chk(lib().mk_decode_step_noalloc(g, d_tokens, d_positions, ctypes.byref(kv), d_logits, stream or None),
+         "mk_decode_step_noalloc")
 
 
 def mk_capture_lpt_graph(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int) -> int:

@@ -896,6 +896,7 @@ void layout(Graph& g) {
   g.off_invfreq = take((int64_t)(D / 2) * 8);
   g.off_geom = take(sizeof(Geom));
   g.off_ops = take((int64_t)g.ops.size() * sizeof(OpDesc));
+  g.off_ops_static = take((int64_t)g.ops.size() * sizeof(OpDesc));
   g.off_tasks = take((int64_t)g.tasks.size() * sizeof(Task));
   g.off_events = take((int64_t)std::max<size_t>(1, g.events.size()) * sizeof(Event));
   g.off_wloff = take((int64_t)g.wl_off.size() * 4);

@@ -78,6 +78,7 @@ struct Graph {
   std::vector<CopyJob> copies;
   int64_t arena_bytes = 0, scratch_bytes = 0, trace_bytes = 0;
   int64_t off_geom = 0, off_ops = 0, off_tasks = 0, off_events = 0, off_wloff = 0, off_wlids = 0, off_invfreq = 0;
+  int64_t off_ops_static = 0;  // the operator table again, its buffers in the library's static scratch
   int64_t off_counters = 0, off_status = 0, off_progress = 0, off_arrive = 0, off_state_end = 0, off_cand = 0;
   int64_t off_route_hist = -1;  // routed experts: expert choice history (kRouteHistSteps steps), else -1
   int64_t weight_bytes_step = 0;
@@ -133,4 +134,6 @@ struct mk_graph {
   uint64_t budget_ticks = 0;
   int32_t last_steps = 0;   // steps of the last launch (mk_read_routing)
   uint32_t last_tag0 = 0;   // data tag of that launch's first step
+  void* static_scr = nullptr;  // the library's static scratch on this graph's device, when the graph fits it
+  bool last_static = false;    // the last step ran on the static scratch (mk_decode_step_noalloc)
 };

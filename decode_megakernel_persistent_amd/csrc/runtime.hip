@@ -19,6 +19,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -356,6 +357,23 @@ static int kernel_variant(const Graph& G) { return G.gemv == MK_GEMV_MFMA ? kMfm
 
 using namespace mk;
 
+// ---------------------------------------------------------------- static scratch
+// The scratch of mk_decode_step_noalloc: a file-scope device array, one copy
+// on every GPU the library runs on, held until the process ends.  Host code
+// never uses its name as an address: static_scratch() looks the device copy
+// up once per device with hipGetSymbolAddress (at weight loading, the device
+// current) and keeps the pointer.
+static constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Clear n_words words of a scratch state region (counters, status, progress,
+// arrival counters), the status word `none_word` set to 0xFFFFFFFF.  A kernel
+// rather than a memset, so that a caller may capture the call in a graph.
+__global__ void __launch_bounds__(256) mk_clear_state(uint32_t* p, uint32_t n_words, uint32_t none_word) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n_words; i += gridDim.x * 256u)
+    p[i] = i == none_word ? 0xFFFFFFFFu : 0u;
+}
+
 namespace {
 
 #define HIPCHK(x)                                                                   \
@@ -400,6 +418,34 @@ std::string tensor_name_list(const mk_model_shape& s, std::vector<std::pair<std:
   return "";
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+uint32_t g_static_tag[kMaxDevices] = {};  // next data tag on each device's static scratch (0: never used)
+
+// Device address of the static scratch on device `dev` (the current device).
+mk_status static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("static scratch: device index out of range");
+    return MK_ERR_ARG;
+  }
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error(std::string("static scratch: hipGetSymbolAddress failed: ") + hipGetErrorString(e));
+      return MK_ERR_HIP;
+    }
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return MK_OK;
+}
+
+// The scratch the graph's last step ran on (what mk_check and the readers read).
+char* active_scratch(const mk_graph* g) { return (char*)(g->last_static ? g->static_scr : g->scratch); }
+
 int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return 0;
@@ -410,22 +456,24 @@ int device_cu_count() {
 }
 
 // Kernel arguments of one launch (epoch and tag taken from the graph handle).
+// With on_static, the step runs on the library's static scratch and the
+// operator table whose buffers point into it (mk_decode_step_noalloc).
 StepArgs step_args(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
-                   float* d_logits, int32_t* d_tokens_out, int32_t n_steps) {
+                   float* d_logits, int32_t* d_tokens_out, int32_t n_steps, bool on_static = false) {
   Graph& G = *g->G;
   char* arena = (char*)g->arena;
-  char* scratch = (char*)g->scratch;
+  char* scr = (char*)(on_static ? g->static_scr : g->scratch);
   StepArgs a;
   std::memset(&a, 0, sizeof a);
   a.geom = (const Geom*)(arena + G.off_geom);
-  a.ops = (const OpDesc*)(arena + G.off_ops);
+  a.ops = (const OpDesc*)(arena + (on_static ? G.off_ops_static : G.off_ops));
   a.tasks = (const Task*)(arena + G.off_tasks);
   a.events = (const Event*)(arena + G.off_events);
   a.wl_off = (const int32_t*)(arena + G.off_wloff);
   a.wl_ids = (const int32_t*)(arena + G.off_wlids);
-  a.counters = (u32*)(scratch + G.off_counters);
-  a.status = (u32*)(scratch + G.off_status);
-  a.progress = (u32*)(scratch + G.off_progress);
+  a.counters = (u32*)(scr + G.off_counters);
+  a.status = (u32*)(scr + G.off_status);
+  a.progress = (u32*)(scr + G.off_progress);
   a.tokens = d_tokens;
   a.positions = d_positions;
   a.kv_k = (uint16_t*)kv->k;
@@ -447,8 +495,8 @@ StepArgs step_args(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positi
   a.run_base = g->persistent_steps;
   a.step = 0;
   a.tokens_out = d_tokens_out;
-  a.cand = (u64*)(scratch + G.off_cand);
-  a.route_hist = G.off_route_hist >= 0 ? (u64*)(scratch + G.off_route_hist) : nullptr;
+  a.cand = (u64*)(scr + G.off_cand);
+  a.route_hist = G.off_route_hist >= 0 ? (u64*)(scr + G.off_route_hist) : nullptr;
   return a;
 }
 
@@ -505,6 +553,42 @@ mk_status launch_lpt(mk_graph* g, StepArgs a, hipStream_t stream) {
     }
   }
   return MK_OK;
+}
+
+// Enqueue one launch (persistent: the worker grid and the dispatch wavefront;
+// launch-per-task: its launch sequence) with the given arguments.
+mk_status launch_step(mk_graph* g, StepArgs& a, bool multi, hipStream_t stream) {
+  Graph& G = *g->G;
+  const int nb = kernel_variant(G);
+  if (g->mode == MK_PERSISTENT) {
+    hipStream_t side = (hipStream_t)g->side_stream;
+    const bool watch = !G.opts.no_watchdog;
+    // The worker grid is submitted before the dispatch wavefront, which
+    // still runs beside it (its stream waits only on ev_a, recorded ahead of
+    // the workers).  Submitted the other way round, the step measured ~0.8%
+    // slower.
+    if (watch) HIPCHK(hipEventRecord((hipEvent_t)g->ev_a, stream));
+    void* kargs[] = {&a};
+    hipError_t e = hipLaunchCooperativeKernel(worker_fn(nb, multi), dim3(G.W), dim3(NT), kargs, kLdsBytes, stream);
+    if (e == hipErrorCooperativeLaunchTooLarge) {
+      (void)hipGetLastError();
+      set_error("mk_decode_step: " + std::to_string(G.W) + " workers cannot be co-resident on this device");
+      return MK_ERR_NOT_RESIDENT;
+    }
+    if (e != hipSuccess) {
+      set_error(std::string("mk_decode_step: cooperative launch failed: ") + hipGetErrorString(e));
+      return MK_ERR_HIP;
+    }
+    if (watch) {
+      HIPCHK(hipStreamWaitEvent(side, (hipEvent_t)g->ev_a, 0));
+      hipLaunchKernelGGL(mk_dispatch, dim3(1), dim3(64), 0, side, a);
+      HIPCHK(hipGetLastError());
+      HIPCHK(hipEventRecord((hipEvent_t)g->ev_b, side));
+      HIPCHK(hipStreamWaitEvent(stream, (hipEvent_t)g->ev_b, 0));
+    }
+    return MK_OK;
+  }
+  return launch_lpt(g, a, stream);
 }
 
 }  // namespace
@@ -673,7 +757,7 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
     g->ev_b = eb;
   }
   char* arena = (char*)d_arena;
-  char* scratch = (char*)d_scratch;
+  char* scr = (char*)d_scratch;
   // ---- weights
   for (const CopyJob& cj : G.copies) {
     const mk_tensor* t = have[cj.tensor];
@@ -710,10 +794,13 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   Geom ge = G.geom;
   ge.inv_freq = (const double*)(arena + G.off_invfreq);
   HIPCHK(hipMemcpy(arena + G.off_geom, &ge, sizeof ge, hipMemcpyHostToDevice));
+  // the operator table, its buffers in `base` (the caller's scratch, or the
+  // library's static scratch for mk_decode_step_noalloc)
   std::vector<OpDesc> od(G.ops.size());
+  auto op_table = [&](char* base) {
   auto bufp = [&](int32_t id) -> uint64_t* {
     if (id < 0 || G.bufs[id].off < 0) return nullptr;
-    return (uint64_t*)(scratch + G.bufs[id].off);
+    return (uint64_t*)(base + G.bufs[id].off);
   };
   for (size_t i = 0; i < G.ops.size(); ++i) {
     const OpInst& o = G.ops[i];
@@ -736,21 +823,33 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
     d.aux = bufp(o.aux_buf);
     d.aux2 = bufp(o.aux2_buf);
     if (o.aux_buf == -3)  // attention arrival counters of layer o.layer
-      d.aux = (uint64_t*)(scratch + G.off_arrive +
+      d.aux = (uint64_t*)(base + G.off_arrive +
                           (int64_t)o.layer * G.B * G.shape.n_kv_heads * kCounterStride * 4);
   }
+  };
+  op_table(scr);
   HIPCHK(hipMemcpy(arena + G.off_ops, od.data(), od.size() * sizeof(OpDesc), hipMemcpyHostToDevice));
+  // the same table over the static scratch, when the graph fits it
+  g->static_scr = nullptr;
+  if (G.scratch_bytes <= (int64_t)kStaticScratchBytes) {
+    void* sp = nullptr;
+    const mk_status rs = static_scratch(dev, &sp);
+    if (rs != MK_OK) return rs;
+    op_table((char*)sp);
+    HIPCHK(hipMemcpy(arena + G.off_ops_static, od.data(), od.size() * sizeof(OpDesc), hipMemcpyHostToDevice));
+    g->static_scr = sp;
+  }
   HIPCHK(hipMemcpy(arena + G.off_tasks, G.tasks.data(), G.tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
   if (!G.events.empty())
     HIPCHK(hipMemcpy(arena + G.off_events, G.events.data(), G.events.size() * sizeof(Event), hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(arena + G.off_wloff, G.wl_off.data(), G.wl_off.size() * 4, hipMemcpyHostToDevice));
   if (!G.wl_ids.empty())
     HIPCHK(hipMemcpy(arena + G.off_wlids, G.wl_ids.data(), G.wl_ids.size() * 4, hipMemcpyHostToDevice));
-  HIPCHK(hipMemsetAsync(scratch, 0, (size_t)G.scratch_bytes, stream));
+  HIPCHK(hipMemsetAsync(scr, 0, (size_t)G.scratch_bytes, stream));
   if (G.trace_bytes > 0) HIPCHK(hipMemsetAsync(d_trace, 0, (size_t)G.trace_bytes, stream));
   HIPCHK(hipStreamSynchronize(stream));
   const u32 none = 0xFFFFFFFFu;
-  HIPCHK(hipMemcpy(scratch + G.off_status + ST_MIN_TASK * 4, &none, 4, hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(scr + G.off_status + ST_MIN_TASK * 4, &none, 4, hipMemcpyHostToDevice));
   int wcr = 0;
   HIPCHK(hipDeviceGetAttribute(&wcr, hipDeviceAttributeWallClockRate, dev));
   const int64_t us = G.opts.spin_timeout_us > 0 ? G.opts.spin_timeout_us : 2000000;
@@ -778,6 +877,7 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   g->scratch = d_scratch;
   g->trace = d_trace;
   g->loaded = true;
+  g->last_static = false;
   g->epoch = 0;
   g->persistent_steps = 0;
   g->tag = 1;
@@ -831,45 +931,69 @@ mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d
   if (!kv_ok(G, kv, "mk_decode_step")) return MK_ERR_ARG;
   hipStream_t stream = (hipStream_t)stream_;
   StepArgs a = step_args(g, d_tokens, d_positions, kv, d_logits, d_tokens_out, n_steps);
-  const int nb = kernel_variant(G);
   if (a.trace_on == 1) HIPCHK(hipMemsetAsync(a.status + ST_TICKET, 0, 2 * sizeof(u32), stream));
-  if (g->mode == MK_PERSISTENT) {
-    hipStream_t side = (hipStream_t)g->side_stream;
-    const bool watch = !G.opts.no_watchdog;
-    // The worker grid is submitted before the dispatch wavefront, which
-    // still runs beside it (its stream waits only on ev_a, recorded ahead of
-    // the workers).  Submitted the other way round, the step measured ~0.8%
-    // slower.
-    if (watch) HIPCHK(hipEventRecord((hipEvent_t)g->ev_a, stream));
-    void* kargs[] = {&a};
-    const bool multi = n_steps > 1 || d_tokens_out != nullptr;
-    hipError_t e = hipLaunchCooperativeKernel(worker_fn(nb, multi), dim3(G.W), dim3(NT), kargs, kLdsBytes, stream);
-    if (e == hipErrorCooperativeLaunchTooLarge) {
-      (void)hipGetLastError();
-      set_error("mk_decode_step: " + std::to_string(G.W) + " workers cannot be co-resident on this device");
-      return MK_ERR_NOT_RESIDENT;
-    }
-    if (e != hipSuccess) {
-      set_error(std::string("mk_decode_step: cooperative launch failed: ") + hipGetErrorString(e));
-      return MK_ERR_HIP;
-    }
-    if (watch) {
-      HIPCHK(hipStreamWaitEvent(side, (hipEvent_t)g->ev_a, 0));
-      hipLaunchKernelGGL(mk_dispatch, dim3(1), dim3(64), 0, side, a);
-      HIPCHK(hipGetLastError());
-      HIPCHK(hipEventRecord((hipEvent_t)g->ev_b, side));
-      HIPCHK(hipStreamWaitEvent(stream, (hipEvent_t)g->ev_b, 0));
-    }
-  } else {
-    const mk_status rc = launch_lpt(g, a, stream);
-    if (rc != MK_OK) return rc;
-  }
+  const mk_status rc = launch_step(g, a, n_steps > 1 || d_tokens_out != nullptr, stream);
+  if (rc != MK_OK) return rc;
+  g->last_static = false;
   g->last_steps = n_steps;
   g->last_tag0 = a.tag;
   g->epoch += (uint32_t)n_steps;
   if (g->mode == MK_PERSISTENT) g->persistent_steps += (uint32_t)n_steps;
   g->tag += (uint32_t)n_steps;
   if (g->tag == 0) g->tag = 1;
+  return MK_OK;
+}
+
+mk_status mk_decode_step_noalloc(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions,
+                                 const mk_kv_cache* kv, float* d_logits, void* stream_) {
+  if (!g || !g->G) {
+    set_error("mk_decode_step_noalloc: null graph");
+    return MK_ERR_ARG;
+  }
+  Graph& G = *g->G;
+  if (G.scratch_bytes > (int64_t)kStaticScratchBytes) {
+    set_error("mk_decode_step_noalloc: the graph needs " + std::to_string(G.scratch_bytes) +
+              " bytes of scratch; the static scratch holds " + std::to_string(kStaticScratchBytes));
+    return MK_ERR_ARG;
+  }
+  if (!g->loaded || !g->static_scr) {
+    set_error("mk_decode_step_noalloc: weights not loaded");
+    return MK_ERR_STATE;
+  }
+  if (!d_tokens || !d_positions || !kv || !d_logits) {
+    set_error("mk_decode_step_noalloc: null argument");
+    return MK_ERR_ARG;
+  }
+  if (!kv_ok(G, kv, "mk_decode_step_noalloc")) return MK_ERR_ARG;
+  hipStream_t stream = (hipStream_t)stream_;
+  // this call's data tag on the device's static scratch: never one that a
+  // word left there by an earlier call carries (tags only grow; when they
+  // would reach the reserved graph tag, the whole array is cleared first)
+  uint32_t tag;
+  bool clear_all = false;
+  {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    uint32_t& next = g_static_tag[g->device];
+    if (next == 0 || next >= kGraphTag - 1u) {
+      clear_all = next != 0;
+      next = 1;
+    }
+    tag = next++;
+  }
+  const uint32_t none_word = (uint32_t)((G.off_status + ST_MIN_TASK * 4) / 4);
+  const uint64_t words = (clear_all ? (uint64_t)kStaticScratchBytes : (uint64_t)G.off_state_end) / 4;
+  hipLaunchKernelGGL(mk_clear_state, dim3((unsigned)std::min<uint64_t>(1024, (words + 255) / 256)), dim3(256), 0,
+                     stream, (uint32_t*)g->static_scr, (uint32_t)words, none_word);
+  HIPCHK(hipGetLastError());
+  StepArgs a = step_args(g, d_tokens, d_positions, kv, d_logits, nullptr, 1, true);
+  a.epoch = 0;
+  a.run_base = 0;
+  a.tag = tag;
+  const mk_status rc = launch_step(g, a, false, stream);
+  if (rc != MK_OK) return rc;
+  g->last_static = true;
+  g->last_steps = 1;
+  g->last_tag0 = tag;
   return MK_OK;
 }
 
@@ -941,6 +1065,7 @@ mk_status mk_lpt_graph_launch(mk_lpt_graph* lg, void* stream) {
   lg->g->epoch += 1;
   lg->g->last_steps = 1;
   lg->g->last_tag0 = kGraphTag;
+  lg->g->last_static = false;
   return MK_OK;
 }
 
@@ -956,8 +1081,9 @@ mk_status mk_check(mk_graph* g) {
     return MK_ERR_STATE;
   }
   Graph& G = *g->G;
+  char* scr = active_scratch(g);
   u32 st[ST_WORDS];
-  HIPCHK(hipMemcpy(st, (char*)g->scratch + G.off_status, sizeof st, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(st, scr + G.off_status, sizeof st, hipMemcpyDeviceToHost));
   if (st[ST_ERROR] == ERR_NONE) return MK_OK;
   std::string msg;
   mk_status rc = MK_ERR_TIMEOUT;
@@ -974,7 +1100,7 @@ mk_status mk_check(mk_graph* g) {
              " workers finish";
     } else {
       const uint64_t addr = ((uint64_t)st[ST_ADDR_HI] << 32) | st[ST_ADDR_LO];
-      const uint64_t base = (uint64_t)(uintptr_t)g->scratch;
+      const uint64_t base = (uint64_t)(uintptr_t)scr;
       std::string where = "?";
       for (const Buffer& b : G.bufs)
         if (b.off >= 0 && addr >= base + b.off && addr < base + b.off + b.words * 8)
@@ -984,14 +1110,14 @@ mk_status mk_check(mk_graph* g) {
     }
     if (st[ST_ADDR_LO] | st[ST_ADDR_HI]) {
       const uint64_t addr = ((uint64_t)st[ST_ADDR_HI] << 32) | st[ST_ADDR_LO];
-      const uint64_t base = (uint64_t)(uintptr_t)g->scratch;
+      const uint64_t base = (uint64_t)(uintptr_t)scr;
       for (const Buffer& b : G.bufs)
         if (b.off >= 0 && addr >= base + b.off && addr < base + b.off + b.words * 8)
           msg += "; stale word " + b.name + "[" + std::to_string((addr - base - b.off) / 8) + "]";
     }
     {
       std::vector<u32> prog((size_t)G.W + 1);
-      if (hipMemcpy(prog.data(), (char*)g->scratch + G.off_progress, prog.size() * 4, hipMemcpyDeviceToHost) ==
+      if (hipMemcpy(prog.data(), scr + G.off_progress, prog.size() * 4, hipMemcpyDeviceToHost) ==
           hipSuccess) {
         std::vector<std::pair<u32, int>> stuck;
         for (int w = 0; w < G.W; ++w)
@@ -1024,13 +1150,17 @@ mk_status mk_check(mk_graph* g) {
     msg = "device error " + std::to_string(st[ST_ERROR]);
     rc = MK_ERR_STATE;
   }
-  // reset the event state so that the next step can run
-  HIPCHK(hipMemset((char*)g->scratch + G.off_counters, 0, (size_t)(G.off_state_end - G.off_counters)));
+  // reset the event state so that the next step can run (a step on the
+  // static scratch starts from a cleared state anyway; the graph's own
+  // scratch keeps its epoch otherwise)
+  HIPCHK(hipMemset(scr + G.off_counters, 0, (size_t)(G.off_state_end - G.off_counters)));
   HIPCHK(hipDeviceSynchronize());
   const u32 none = 0xFFFFFFFFu;
-  HIPCHK(hipMemcpy((char*)g->scratch + G.off_status + ST_MIN_TASK * 4, &none, 4, hipMemcpyHostToDevice));
-  g->epoch = 0;
-  g->persistent_steps = 0;
+  HIPCHK(hipMemcpy(scr + G.off_status + ST_MIN_TASK * 4, &none, 4, hipMemcpyHostToDevice));
+  if (!g->last_static) {
+    g->epoch = 0;
+    g->persistent_steps = 0;
+  }
   set_error("mk_check: " + msg);
   return rc;
 }
@@ -1047,7 +1177,7 @@ mk_status mk_read_trace(mk_graph* g, mk_trace_rec* host_buf, int64_t cap, int64_
   }
   u32 cnt = (u32)G.tasks.size();  // timing trace: one slot per task
   if (G.opts.trace == 1)
-    HIPCHK(hipMemcpy(&cnt, (char*)g->scratch + G.off_status + ST_TRACE_N * 4, 4, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(&cnt, active_scratch(g) + G.off_status + ST_TRACE_N * 4, 4, hipMemcpyDeviceToHost));
   int64_t m = std::min<int64_t>({(int64_t)cnt, cap, (int64_t)G.tasks.size()});
   if (m > 0 && host_buf) HIPCHK(hipMemcpy(host_buf, g->trace, (size_t)m * sizeof(mk_trace_rec), hipMemcpyDeviceToHost));
   *n = (int64_t)cnt;
@@ -1083,7 +1213,7 @@ mk_status mk_read_routing(mk_graph* g, int32_t step, int32_t* experts, float* we
   }
   const size_t slot = (size_t)(step % kRouteHistSteps);
   std::vector<u64> rec((size_t)n);
-  HIPCHK(hipMemcpy(rec.data(), (char*)g->scratch + G.off_route_hist + slot * (size_t)n * 8, (size_t)n * 8,
+  HIPCHK(hipMemcpy(rec.data(), active_scratch(g) + G.off_route_hist + slot * (size_t)n * 8, (size_t)n * 8,
                    hipMemcpyDeviceToHost));
   for (int64_t i = 0; i < n; ++i) {
     experts[i] = (int32_t)(uint32_t)rec[(size_t)i];
@@ -1104,7 +1234,7 @@ mk_status mk_read_routing(mk_graph* g, int32_t step, int32_t* experts, float* we
         set_error("mk_read_routing: router buffer of layer " + std::to_string(l) + " not found");
         return MK_ERR_STATE;
       }
-      HIPCHK(hipMemcpy(w.data(), (char*)g->scratch + buf->off, (size_t)be * 8, hipMemcpyDeviceToHost));
+      HIPCHK(hipMemcpy(w.data(), active_scratch(g) + buf->off, (size_t)be * 8, hipMemcpyDeviceToHost));
       for (int64_t i = 0; i < be; ++i) {
         if ((uint32_t)(w[(size_t)i] >> 32) != want) {
           set_error("mk_read_routing: router logits of layer " + std::to_string(l) + " are not the last step's");
@@ -1130,7 +1260,8 @@ mk_status mk_read_counters(mk_graph* g, uint32_t* host_counters, int64_t cap) {
     return MK_ERR_ARG;
   }
   std::vector<u32> raw((size_t)ne * kSubCounters * kCounterStride);
-  if (ne > 0) HIPCHK(hipMemcpy(raw.data(), (char*)g->scratch + G.off_counters, raw.size() * 4, hipMemcpyDeviceToHost));
+  if (ne > 0)
+    HIPCHK(hipMemcpy(raw.data(), active_scratch(g) + G.off_counters, raw.size() * 4, hipMemcpyDeviceToHost));
   for (int64_t e = 0; e < ne; ++e) {
     u32 s = 0;
     for (int k = 0; k < kSubCounters; ++k) s += raw[((size_t)e * kSubCounters + k) * kCounterStride];

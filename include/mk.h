@@ -222,6 +222,23 @@ mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_
 mk_status mk_decode_steps(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
                           float* d_logits, int32_t* d_tokens_out, int32_t n_steps, void* stream);
 
+/* mk_decode_step for callers that cannot allocate device memory around a
+ * step (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same step, run on a scratch area the library holds
+ * in a static device array of 64 MiB, one per GPU, kept until the process
+ * ends, instead of the scratch given to mk_load_weights.  It calls no
+ * allocating routine.  Graphs whose scratch (mk_workspace_size) exceeds 64 MiB
+ * are rejected with MK_ERR_ARG; the batch-1 decoders up to the 8B shape fit.
+ * Every call clears the event state it needs (a fill kernel on `stream`) and
+ * takes a data tag no earlier call on the device used, so calls may follow
+ * each other with different graphs; calls that overlap on one GPU (other
+ * streams, other threads) race on the shared array.  Afterwards mk_check,
+ * mk_read_trace, mk_read_counters and mk_read_routing read this call's state.
+ * The graph's own scratch and its step count are left as they were.
+ * Errors: as mk_decode_step. */
+mk_status mk_decode_step_noalloc(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions,
+                                 const mk_kv_cache* kv, float* d_logits, void* stream);
+
 /* Launch-per-task mode captured once into a HIP graph and replayed: the same
  * task bodies and launch sequence as mode MK_LAUNCH_PER_TASK, without the
  * host's per-launch cost.  This is the pages' CUDA-Graphs comparison point for
