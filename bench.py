@@ -4,13 +4,16 @@
     python bench.py [--gpus 1] [--steps 32] [--warmup 2] [--workload qwen3-8b]
 
 One step is one full decode step of the workload (embedding, every layer's
-RMSNorm/QKV/QK-norm+RoPE+KV-append/attention/merge/O/SwiGLU MLP, final norm
-and lm_head) on synthetic inputs already resident in HBM.  Prints one JSON
-line: ms/token (mean over the timed steps, per-step HIP events on the
-launching stream) and the algorithmic HBM bandwidth of the step (weights read
-+ KV read + KV written + logits, divided by the step time) against MI355X's
-8 TB/s peak, the same step in launch-per-task mode, and the oracle's ms/token
-on the host cores over a bounded sample.
+RMSNorm/QKV/QK-norm+RoPE+KV-append/attention/merge/O/SwiGLU MLP or routed
+experts, final norm and lm_head) on synthetic inputs already resident in HBM.
+Prints one JSON line: ms/token (median over the timed steps, mean beside it;
+per-step HIP events on the stream the worker kernel is launched on) and the
+algorithmic HBM bandwidth of the step (weights read -- for routed experts the
+distinct experts the GPU chose, read back per step -- plus KV read, KV
+written and logits, over the step time) against MI355X's 8 TB/s peak and the
+box's measured streaming-read rate; the same step in launch-per-task mode,
+eager and replayed as a HIP graph; greedy steps in one launch; the paged KV
+layout; and the oracle's ms/token on the host cores over a bounded sample.
 """
 
 from __future__ import annotations
@@ -31,35 +34,58 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mk_worker_qwen3-8b_b1_traffic.txt")
 
 
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(shape, batch: int, positions: np.ndarray, weight_bytes: int) -> float:
-    """Bytes one step must move: weights read, embedding rows, norm gains,
-    KV read (positions 0..p for each sequence and layer), KV written, logits."""
+def kv_bytes(shape, batch: int, positions: np.ndarray) -> float:
+    """KV read (positions 0..p of each sequence and layer) plus KV written."""
     s = shape
     kv_row = 2 * s.n_kv_heads * s.head_dim * 2  # K and V of one position, one layer
-    kv_read = sum(int(p) + 1 for p in positions) * kv_row * s.n_layers
-    kv_write = batch * kv_row * s.n_layers
+    return float(sum(int(p) + 1 for p in positions) * kv_row * s.n_layers + batch * kv_row * s.n_layers)
+
+
+def algorithmic_bytes(shape, batch: int, positions: np.ndarray, weight_bytes: float) -> float:
+    """Bytes one step must move: weights read, embedding rows, norm gains, KV
+    read and written, logits."""
+    s = shape
     gains = s.n_layers * (2 * s.hidden + 2 * s.head_dim) * 4 + s.hidden * 4
     embed = batch * s.hidden * 2
     logits = batch * s.vocab * 4
-    return float(weight_bytes + embed + gains + kv_read + kv_write + logits)
+    return float(weight_bytes + embed + gains + kv_bytes(s, batch, positions) + logits)
 
 
-def time_steps(sess, tok_dev, pos0: np.ndarray, warmup: int, steps: int):
+def expert_bytes(shape, experts: np.ndarray) -> float:
+    """Weight bytes of the distinct routed experts chosen in each layer
+    (experts [L][B][top_k] from the GPU's routing record)."""
+    per_expert = 3 * shape.expert_intermediate * shape.hidden * 2
+    return float(sum(len(np.unique(experts[l])) for l in range(experts.shape[0])) * per_expert)
+
+
+def time_steps(sess, tok_dev, pos0: np.ndarray, warmup: int, steps: int, routed: bool = False, noalloc=False):
     """Per-step HIP events on the stream the step is launched on (the
     session's stream is torch's current stream), bracketing exactly the
-    decode_step enqueue; the next step's token/position copies sit outside."""
+    decode_step enqueue; token/position copies sit outside.  Routed models
+    synchronise after each step to read the GPU's expert choice (the events
+    still time only the launch)."""
     import torch
+    import decode_megakernel_persistent_amd as mk
     st = torch.cuda.current_stream()
     pos = torch.as_tensor(pos0.astype(np.int32), device=sess.device)
-    pos_list = []
+    pos_list, experts = [], []
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def enqueue():
+        if noalloc:
+            mk.mk_decode_step_noalloc(sess.g, sess.tokens.data_ptr(), sess.positions.data_ptr(), sess.kv,
+                                      sess.logits.data_ptr(), sess.stream)
+        else:
+            sess.enqueue()
     torch.cuda.synchronize()
     for i in range(warmup):
         sess.tokens.copy_(tok_dev[i % tok_dev.shape[0]])
         sess.positions.copy_(pos + i)
-        sess.enqueue()
+        enqueue()
     torch.cuda.synchronize()
     sess.check()
     t0 = time.perf_counter()
@@ -69,13 +95,41 @@ def time_steps(sess, tok_dev, pos0: np.ndarray, warmup: int, steps: int):
         sess.positions.copy_(pos + k)
         pos_list.append(pos0 + k)
         ev[i][0].record(st)
-        sess.enqueue()
+        enqueue()
         ev[i][1].record(st)
+        if routed:
+            torch.cuda.synchronize()
+            experts.append(sess.read_routing(0, with_logits=False)[0])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sess.check()
     times = [a.elapsed_time(b) for a, b in ev]
-    return times, pos_list, wall
+    return times, pos_list, experts, wall
+
+
+def stream_probe(gib: float = 4.0, reps: int = 5) -> float:
+    """The box's streaming-read rate (GB/s): a plain 16-byte-load read of a
+    buffer far larger than the caches, median of `reps` timed reads."""
+    import torch
+    import decode_megakernel_persistent_amd as mk
+    n = int(gib * (1 << 30))
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    blocks = 256 * 8
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    times = []
+    for r in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        mk.mk_stream_read(buf.data_ptr(), n, sink.data_ptr(), blocks, st.cuda_stream)
+        b.record(st)
+        torch.cuda.synchronize()
+        if r:
+            times.append(a.elapsed_time(b))
+    del buf
+    torch.cuda.empty_cache()
+    return n / (statistics.median(times) * 1e-3) / 1e9
 
 
 def calibrate_copy(mib: int, reps: int = 3) -> None:
@@ -89,7 +143,18 @@ def calibrate_copy(mib: int, reps: int = 3) -> None:
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"[bench] calibration copies: {reps} x {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
+    log(f"calibration copies: {reps} x {mib} MiB read + {mib} MiB written")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, weights, kv_k, kv_v, tokens0, pos0, budget_s: float):
@@ -112,6 +177,12 @@ def cpu_baseline(w, weights, kv_k, kv_v, tokens0, pos0, budget_s: float):
     return el * 1000.0 / (n * w.batch), n, threads
 
 
+def activation_bytes(sess) -> float:
+    """Bytes of inter-task activations one step writes and reads back (the
+    scratch past the event state, written once and read once at least)."""
+    return 2.0 * float(sess.stats.scratch_bytes)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,8 +193,15 @@ def main():
     ap.add_argument("--no-lpt", action="store_true")
     ap.add_argument("--multi-steps", type=int, default=16,
                     help="also time mk_decode_steps with this many greedy steps per launch (0 = skip)")
+    ap.add_argument("--paged", type=int, default=16, metavar="PAGE",
+                    help="also time the step on a paged KV cache with this page size (0 = skip)")
+    ap.add_argument("--no-stream-probe", action="store_true")
+    ap.add_argument("--attribution", action="store_true",
+                    help="also run one step with the timing trace: per-layer split and the five-bucket attribution")
+    ap.add_argument("--timeline-json", default="", help="with --attribution: write the Perfetto timeline here")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--profile-only", action="store_true", help="persistent steps only (for profilers)")
+    ap.add_argument("--profile-only", action="store_true", help="one mode's steps only (for profilers)")
+    ap.add_argument("--profile-mode", choices=["persistent", "lpt"], default="persistent")
     ap.add_argument("--no-watchdog", action="store_true",
                     help="launch no dispatch wavefront (for counter runs, which serialise dispatches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -138,62 +216,76 @@ def main():
     import dataclasses
     import synth
     import decode_megakernel_persistent_amd as mk
+    from decode_megakernel_persistent_amd import timeline
 
     base = synth.WORKLOADS[args.workload]
     # capacity for every position the run writes
-    w = dataclasses.replace(base, steps=args.warmup + args.steps)
+    w = dataclasses.replace(base, steps=args.warmup + args.steps + max(args.multi_steps, 0))
     s = w.shape
+    routed = s.n_experts > 0
     t_setup = time.perf_counter()
     weights = synth.weights(s)
     lens = synth.lengths(w)
     L, B, Hkv, cap, D = s.n_layers, w.batch, s.n_kv_heads, w.capacity, s.head_dim
     kv_k = np.zeros((L, B, Hkv, cap, D), dtype=np.uint16)
     kv_v = np.zeros_like(kv_k)
-    if w.prompt:
-        # the tiny workload's prompt is prefilled by the oracle in the parity
-        # tests; for timing, random cache entries of the same length stand in
-        synth.fill_kv(s, B, cap, lens, kv_k, kv_v)
-    else:
-        synth.fill_kv(s, B, cap, lens, kv_k, kv_v)
+    # random cache entries stand in for the tiny workload's oracle-prefilled prompt
+    synth.fill_kv(s, B, cap, lens, kv_k, kv_v)
     ntok = args.warmup + args.steps
     toks = synth.tokens(w, ntok)  # [B, ntok]
-    print(f"[bench] inputs ready in {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    log(f"inputs ready in {time.perf_counter() - t_setup:.1f}s")
 
-    sess = mk.Session(s, B, cap, mk.make_opts(mode=mk.MK_PERSISTENT, no_watchdog=int(args.no_watchdog)))
+    mode = mk.MK_LAUNCH_PER_TASK if args.profile_only and args.profile_mode == "lpt" else mk.MK_PERSISTENT
+    sess = mk.Session(s, B, cap, mk.make_opts(mode=mode, no_watchdog=int(args.no_watchdog)))
     sess.load(weights)
     sess.set_kv(kv_k, kv_v)
     tok_dev = torch.as_tensor(toks.T.copy(), device=sess.device)  # [ntok, B]
     pos0 = lens.astype(np.int64)
-    print(f"[bench] graph: {sess.stats.tasks} tasks, {sess.stats.events} events, "
-          f"{sess.stats.workers} workers; loaded in {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    log(f"graph: {sess.stats.tasks} tasks, {sess.stats.events} events, {sess.stats.workers} workers; "
+        f"loaded in {time.perf_counter() - t_setup:.1f}s")
 
-    times, pos_list, wall = time_steps(sess, tok_dev, pos0, args.warmup, args.steps)
+    times, pos_list, experts, wall = time_steps(sess, tok_dev, pos0, args.warmup, args.steps, routed)
     med = statistics.median(times)
     mean = statistics.fmean(times)
-    bytes_steps = [algorithmic_bytes(s, B, p, sess.stats.weight_bytes) for p in pos_list]
+    wbytes = [float(sess.stats.weight_bytes) + (expert_bytes(s, e) if routed else 0.0)
+              for e in (experts if routed else [None] * len(pos_list))]
+    bytes_steps = [algorithmic_bytes(s, B, p, wb) for p, wb in zip(pos_list, wbytes)]
     bytes_mean = statistics.fmean(bytes_steps)
-    # algorithmic bytes per launch / the average launch duration
+    # algorithmic bytes per launch / the average launch duration (the rocprofv3 figure)
     achieved = bytes_mean / (mean * 1e-3) / 1e9
-    print(f"[bench] persistent: mean {mean:.4f} ms/step, median {med:.4f}, {achieved:.0f} GB/s "
-          f"({bytes_mean / 1e9:.3f} GB/step), wall {wall:.3f}s for {args.steps} steps", file=sys.stderr, flush=True)
+    achieved_med = bytes_mean / (med * 1e-3) / 1e9
+    log(f"{'launch-per-task' if mode else 'persistent'}: median {med:.4f} ms/step, mean {mean:.4f}, "
+        f"{achieved:.0f} GB/s ({bytes_mean / 1e9:.3f} GB/step), wall {wall:.3f}s for {args.steps} steps")
     if args.profile_only:
         sess.close()
         if args.calibrate_copy:
             calibrate_copy(args.calibrate_copy)
-        print("[bench] profile run done", file=sys.stderr, flush=True)
+        log("profile run done")
         return
+
+    stream_gbs = None
+    if not args.no_stream_probe:
+        stream_gbs = stream_probe()
+        log(f"streaming read probe: {stream_gbs:.0f} GB/s")
+
+    noalloc = None
+    if sess.stats.scratch_bytes <= 64 << 20:
+        sess.set_kv(kv_k, kv_v)
+        t_n, _, _, _ = time_steps(sess, tok_dev, pos0, args.warmup, args.steps, False, noalloc=True)
+        noalloc = {"median_ms_per_step": round(statistics.median(t_n), 4), "ms_per_step": round(statistics.fmean(t_n), 4)}
+        log(f"static-scratch step (mk_decode_step_noalloc): median {noalloc['median_ms_per_step']:.4f} ms")
 
     lpt = None
     if not args.no_lpt:
         sess.set_kv(kv_k, kv_v)
         sess.set_mode(mk.MK_LAUNCH_PER_TASK)
-        t_l, _, _ = time_steps(sess, tok_dev, pos0, args.warmup, args.steps)
-        mean_l = statistics.fmean(t_l)
-        lpt = {"ms_per_step": round(mean_l, 4), "median_ms": round(statistics.median(t_l), 4),
+        t_l, _, _, _ = time_steps(sess, tok_dev, pos0, args.warmup, args.steps, False)
+        med_l, mean_l = statistics.median(t_l), statistics.fmean(t_l)
+        lpt = {"median_ms_per_step": round(med_l, 4), "ms_per_step": round(mean_l, 4),
                "launches_per_step": int(sess.stats.launches_per_step),
-               "persistent_speedup": round(mean_l / mean, 3),
-               "overhead_share": round(1.0 - mean / mean_l, 4)}
-        print(f"[bench] launch-per-task: mean {mean_l:.4f} ms/step", file=sys.stderr, flush=True)
+               "persistent_speedup": round(med_l / med, 3),
+               "overhead_share": round(1.0 - med / med_l, 4)}
+        log(f"launch-per-task: median {med_l:.4f} ms/step")
         # the same launches captured once into a HIP graph and replayed: what
         # remains of the gap to the persistent kernel is not host launch cost
         h = sess.capture_lpt_graph()
@@ -210,10 +302,9 @@ def main():
         torch.cuda.synchronize()
         sess.check()
         t_g = [a.elapsed_time(b) for a, b in ev[args.warmup:]]
-        mean_g = statistics.fmean(t_g)
-        lpt["graph_ms_per_step"] = round(mean_g, 4)
-        lpt["graph_persistent_speedup"] = round(mean_g / mean, 3)
-        print(f"[bench] launch-per-task as a HIP graph: mean {mean_g:.4f} ms/step", file=sys.stderr, flush=True)
+        lpt["graph_median_ms_per_step"] = round(statistics.median(t_g), 4)
+        lpt["graph_persistent_speedup"] = round(statistics.median(t_g) / med, 3)
+        log(f"launch-per-task as a HIP graph: median {statistics.median(t_g):.4f} ms/step")
         sess.set_mode(mk.MK_PERSISTENT)
 
     multi = None
@@ -236,11 +327,49 @@ def main():
         torch.cuda.synchronize()
         sess.check()
         t_m = [a.elapsed_time(b) for a, b in ev[1:]]
-        per = statistics.fmean(t_m) / n_multi
-        multi = {"steps_per_launch": n_multi, "launches": reps, "ms_per_step": round(per, 4),
+        per = statistics.median(t_m) / n_multi
+        multi = {"steps_per_launch": n_multi, "launches": reps, "median_ms_per_step": round(per, 4),
                  "ms_per_token": round(per / B, 4), "tokens_per_s": round(B * 1000.0 / per, 2),
-                 "speedup_vs_one_step_launches": round(mean / per, 4)}
-        print(f"[bench] multi-step: {n_multi} steps per launch, {per:.4f} ms/step", file=sys.stderr, flush=True)
+                 "speedup_vs_one_step_launches": round(med / per, 4)}
+        log(f"multi-step: {n_multi} steps per launch, {per:.4f} ms/step")
+
+    attribution = None
+    if args.attribution:
+        # one step with the timing trace (clocks only, one record per task)
+        tr = mk.Session(s, B, cap, mk.make_opts(trace=2))
+        tr.load(weights)
+        tr.set_kv(kv_k, kv_v)
+        for i in range(2):
+            tr.step(toks[:, i], pos0 + i)
+            torch.cuda.synchronize()
+            tr.check()
+        recs = tr.read_trace()
+        tasks = mk.mk_get_tasks(tr.g)
+        if args.timeline_json:
+            timeline.to_perfetto(recs, tasks, args.timeline_json)
+        split = timeline.layer_split(recs, tasks)
+        per_op = timeline.attribute(recs, tasks)
+        tr.close()
+        attribution = {
+            "layer_split": split,
+            "per_operator": {k: v for k, v in per_op.items()},
+            "buckets": timeline.buckets(med, lpt["median_ms_per_step"] if lpt else med,
+                                        lpt["graph_median_ms_per_step"] if lpt else None,
+                                        bytes_mean, activation_bytes(sess), stream_gbs, HBM_PEAK_GBS, split)}
+        log("attribution: " + json.dumps(attribution["buckets"]))
+
+    paged = None
+    if args.paged:
+        ps = mk.Session(s, B, cap, mk.make_opts(), page_size=args.paged, spare_pages=B, page_seed=1)
+        ps.load(weights)
+        ps.set_kv(kv_k, kv_v)
+        t_p, _, _, _ = time_steps(ps, tok_dev, pos0, args.warmup, args.steps, False)
+        paged = {"page_size": args.paged, "median_ms_per_step": round(statistics.median(t_p), 4),
+                 "contiguous_median_ms_per_step": round(med, 4),
+                 "paged_over_contiguous": round(statistics.median(t_p) / med, 4)}
+        log(f"paged KV ({args.paged}-row pages): median {statistics.median(t_p):.4f} ms/step")
+        ps.close()
+        del ps
 
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC) and args.workload == "qwen3-8b" and B == 1:
@@ -250,44 +379,51 @@ def main():
         if prof.get("source_hash") == mk.source_hash():
             traffic = int(float(prof["traffic_bytes_per_launch"]))
 
+    stats = sess.stats
+    sess.close()
     cpu = None
     if not args.no_cpu_baseline:
-        sess.close()
         del tok_dev
         torch.cuda.empty_cache()
         ms_cpu, n_cpu, threads = cpu_baseline(w, weights, kv_k, kv_v, toks[:, 0], pos0, args.cpu_budget)
         cpu = {"value": round(ms_cpu, 2), "unit": "ms/token", "cores": int(threads), "kind": "oracle",
+               "cpu_model": cpu_model(),
                "sample": f"{n_cpu} whole decode steps of the same workload (batch {B}) on the host, fp64 oracle"}
-    else:
-        sess.close()
 
+    ctx = int(lens.max())
     out = {
         "metric": "decode ms/token and weight-stream HBM GB/s vs peak, batch 1 (1 GPU)",
-        "value": round(mean / B, 4),
+        "value": round(med / B, 4),
         "unit": "ms/token",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(mean, 4),
-        "median_ms_per_step": round(med, 4),
+        "ms_per_step": round(med, 4),
+        "mean_ms_per_step": round(mean, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}-shaped decoder, batch {B}, KV context {int(lens.max())}",
-                   "batch": B, "context": int(lens.max()), "layers": s.n_layers, "hidden": s.hidden,
-                   "mode": "persistent", "workers": int(sess.stats.workers)},
+        "config": {"workload": f"{args.workload}-shaped decoder, batch {B}, KV context {ctx}"
+                               + (" (ragged)" if w.ragged else ""),
+                   "batch": B, "context": ctx, "layers": s.n_layers, "hidden": s.hidden,
+                   "mode": "persistent", "workers": int(stats.workers)},
         "hbm_gbps": round(achieved, 1),
         "hbm_frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": round(bytes_mean), "kernel": "mk_worker",
-                     "launch_ms": round(mean, 4)},
+                     "launch_ms_mean": round(mean, 4), "achieved_at_median": round(achieved_med, 1),
+                     "stream_probe_gbs": round(stream_gbs, 1) if stream_gbs else None,
+                     "frac_of_stream_probe": round(achieved / stream_gbs, 4) if stream_gbs else None},
         "launch_per_task": lpt,
         "multi_step": multi,
+        "static_scratch_step": noalloc,
+        "paged_kv": paged,
+        "attribution": attribution,
         "cpu_baseline": cpu,
-        "tokens_per_s": round(B * 1000.0 / mean, 2),
+        "tokens_per_s": round(B * 1000.0 / med, 2),
     }
     print(json.dumps(out))
 

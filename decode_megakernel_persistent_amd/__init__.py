@@ -137,6 +137,7 @@ def lib():
         "mk_check_trace": [_vp, _vp, ctypes.c_int64, ctypes.c_uint32, _u32p],
         "mk_read_counters": [_vp, _u32p, ctypes.c_int64],
         "mk_read_routing": [_vp, ctypes.c_int32, _i32p, _vp, _vp, ctypes.c_int64],
+        "mk_stream_read": [_vp, ctypes.c_uint64, _vp, ctypes.c_int32, _vp],
         "mk_simulate": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
                         _i64p, _u32p],
         "mk_graph_stats": [_vp, ctypes.POINTER(mk_stats)],
@@ -167,7 +168,7 @@ EXPORTED = ["mk_build_graph", "mk_workspace_size", "mk_load_weights", "mk_decode
             "mk_capture_lpt_graph", "mk_lpt_graph_launch", "mk_lpt_graph_destroy", "mk_set_mode", "mk_check",
             "mk_read_trace", "mk_check_trace", "mk_read_counters", "mk_read_routing", "mk_simulate", "mk_graph_stats", "mk_dump_graph",
             "mk_get_tasks", "mk_get_events", "mk_get_worker_lists", "mk_get_raw_edges", "mk_destroy_graph",
-            "mk_last_error", "mk_hip_runtime_path"]
+            "mk_last_error", "mk_hip_runtime_path", "mk_stream_read"]
 
 
 def _chk(rc: int, what: str):
@@ -251,6 +252,10 @@ def mk_decode_step_noalloc(g: int, d_tokens: int, d_positions: int, kv: mk_kv_ca
                            stream: int = 0):
     _chk(lib().mk_decode_step_noalloc(g, d_tokens, d_positions, ctypes.byref(kv), d_logits, stream or None),
          "mk_decode_step_noalloc")
+
+
+def mk_stream_read(d_buf: int, nbytes: int, d_sink: int, blocks: int, stream: int = 0):
+    _chk(lib().mk_stream_read(d_buf, nbytes, d_sink, blocks, stream or None), "mk_stream_read")
 
 
 def mk_capture_lpt_graph(g: int, d_tokens: int, d_positions: int, kv: mk_kv_cache, d_logits: int) -> int:

@@ -374,6 +374,25 @@ __global__ void __launch_bounds__(256) mk_clear_state(uint32_t* p, uint32_t n_wo
     p[i] = i == none_word ? 0xFFFFFFFFu : 0u;
 }
 
+// A plain streaming read of `bytes` bytes (16-byte loads, grid-stride): the
+// rate a simple kernel reaches on this machine, reported beside the roofline.
+// Each workgroup leaves the XOR of what it read in sink[block].
+__global__ void __launch_bounds__(512) mk_stream_read_kernel(const mk::u32x4* p, uint64_t n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  for (uint64_t i = blockIdx.x * 512ull + threadIdx.x; i < n16; i += (uint64_t)gridDim.x * 512ull) {
+    const mk::u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  __shared__ uint32_t red[512];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 256; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] ^= red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
 namespace {
 
 #define HIPCHK(x)                                                                   \
@@ -1380,6 +1399,17 @@ void mk_destroy_graph(mk_graph* g) {
   if (g->ev_b) (void)hipEventDestroy((hipEvent_t)g->ev_b);
   delete g->G;
   delete g;
+}
+
+mk_status mk_stream_read(const void* d_buf, uint64_t bytes, uint32_t* d_sink, int32_t blocks, void* stream) {
+  if (!d_buf || !d_sink || blocks <= 0 || bytes % 16 || ((uintptr_t)d_buf & 15)) {
+    set_error("mk_stream_read: bad argument (16-byte aligned buffer, size a multiple of 16, blocks > 0)");
+    return MK_ERR_ARG;
+  }
+  hipLaunchKernelGGL(mk_stream_read_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream, (const mk::u32x4*)d_buf,
+                     bytes / 16, d_sink);
+  HIPCHK(hipGetLastError());
+  return MK_OK;
 }
 
 const char* mk_hip_runtime_path(void) {

@@ -326,6 +326,15 @@ mk_status mk_get_raw_edges(const mk_graph* g, int32_t* rows, int64_t cap, int64_
 void mk_destroy_graph(mk_graph* g);
 const char* mk_last_error(void);
 
+/* Measurement helper: read `bytes` bytes of device memory once (16-byte
+ * loads, `blocks` workgroups of 512 threads, grid-stride), leaving one word
+ * per workgroup in d_sink[blocks].  The streaming-read rate of the box, timed
+ * by the caller, is the practical ceiling the weight roofline is reported
+ * against (survey page on MPK, section 9.3: the step is bounded by the
+ * weight-read roofline).  d_buf 16-byte aligned, bytes a multiple of 16.
+ * Errors: MK_ERR_ARG, MK_ERR_HIP. */
+mk_status mk_stream_read(const void* d_buf, uint64_t bytes, uint32_t* d_sink, int32_t blocks, void* stream);
+
 /* Path of the loaded HIP runtime library (diagnostic: it must be the same one
  * the caller's framework uses). */
 const char* mk_hip_runtime_path(void);

@@ -128,6 +128,44 @@ def test_tiny_timing_trace(tiny):
     assert_reports(reports)
 
 
+def test_timeline_export_from_a_timing_trace(tiny, tmp_path):
+    # the Perfetto timeline of one persistent step: one slice per task on its
+    # worker's track, slices of a worker disjoint, and per-worker run + wait
+    # equal to the worker's span
+    import json
+    from decode_megakernel_persistent_amd import timeline
+    w, prep = tiny
+    sess = mk.Session(w.shape, w.batch, w.capacity, mk.make_opts(trace=2))
+    try:
+        sess.load(prep.weights)
+        sess.set_kv(prep.k0, prep.v0)
+        sess.step(prep.tokens, prep.positions)
+        torch.cuda.synchronize()
+        sess.check()
+        recs = sess.read_trace()
+        tasks = mk.mk_get_tasks(sess.g)
+        p = str(tmp_path / "timeline.json")
+        assert timeline.to_perfetto(recs, tasks, p) == sess.stats.tasks
+        sl = [e for e in json.load(open(p))["traceEvents"] if e["ph"] == "X"]
+        assert sorted(e["args"]["task"] for e in sl) == list(range(sess.stats.tasks))
+        for wk in {e["tid"] for e in sl}:
+            mine = sorted((e["ts"], e["ts"] + e["dur"]) for e in sl if e["tid"] == wk)
+            assert all(a[1] <= b[0] + 0.011 for a, b in zip(mine, mine[1:]))
+        att = timeline.attribute(recs, tasks)
+        t0, t1 = timeline._times_us(recs)
+        ends = {}
+        for i, r in enumerate(recs):
+            ends[int(r["worker"])] = max(ends.get(int(r["worker"]), 0.0), t1[i] - t0.min())
+        total = sum(v["run_us_total"] + v["wait_us_total"] for k, v in att.items() if k != "_span_us")
+        assert abs(total - sum(ends.values())) <= 1e-3 * sum(ends.values()) + 1.0
+        sp = timeline.layer_split(recs, tasks)
+        assert sp["layers"] == w.shape.n_layers and 0 < sp["layer_median_run_us"] <= sp["layer_span_us"]
+        harness.log(f"[timeline] tiny: {len(sl)} slices, layer span {sp['layer_span_us']} us, "
+                    f"median task run per layer {sp['layer_median_run_us']} us")
+    finally:
+        sess.close()
+
+
 def test_tiny_one_chunk_and_many_chunks(tiny):
     w, prep = tiny
     for C in (1, 7):
