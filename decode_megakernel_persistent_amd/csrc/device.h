@@ -183,6 +183,11 @@ DEV float wave_max(float v) {
   return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
+// Slots of the small static LDS block `flags` (int[64]) besides 0..7 (abort,
+// seen, tickets, clocks, trigger state) and 8..44 (GEMV reduction slots).
+constexpr int kFlagEntryClock = 60;  // timing trace: clock at task entry
+constexpr int kFlagWaitClock = 61;   // timing trace: clock when the dependency wait began
+
 // ---------------------------------------------------------------- task context
 struct Ctx {
   const StepArgs* a;
@@ -233,6 +238,8 @@ DEV void poll_dep(Ctx& c) {
   const StepArgs& a = *c.a;
   const int lane = threadIdx.x & 63;
   const int ev = c.t.dep;
+  // timing trace: the clock when the wait begins (the pre-wait loads issued)
+  if (a.trace_on == 2 && lane == 0) c.flags[kFlagWaitClock] = (int)(u32)wall_clock64();
   {
     u32 seen = 0;
     int bad = 0;
@@ -330,8 +337,9 @@ DEV void finish(Ctx& c) {
         r.task = c.id;
         r.worker = (int16_t)c.agent;
         r.xcc = (int16_t)(__builtin_amdgcn_s_getreg(6164) & 0xF);  // HW_REG_XCC_ID[3:0]
-        r.t_start = (u32)c.flags[2];
-        r.t_end = (u32)c.flags[6];
+        // timing trace: the clocks of task entry and of the start of the wait
+        r.t_start = (u32)c.flags[tk ? 2 : kFlagEntryClock];
+        r.t_end = (u32)c.flags[tk ? 6 : kFlagWaitClock];
         r.dep_seen = (u32)c.flags[1];
         r.step = a.epoch;
         r.clk_start = (u32)c.flags[3];

@@ -49,7 +49,10 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
   c.lds = lds;
   c.flags = flags;
   c.pos = pos;
-  if (threadIdx.x == 0) flags[5] = 0;  // not triggered yet (read after the body's barriers)
+  if (threadIdx.x == 0) {
+    flags[5] = 0;  // not triggered yet (read after the body's barriers)
+    if (a.trace_on == 2) flags[kFlagEntryClock] = (int)(u32)wall_clock64();
+  }
   const OpDesc& op = a.ops[c.t.op];
   switch (op.kind) {
     case OP_QKV:

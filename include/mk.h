@@ -145,15 +145,18 @@ typedef struct {
   int32_t reserved;           /* must be zero */
 } mk_kv_cache;
 
-/* One record per executed task (trace mode).  Tickets come from one global
- * atomic counter: start is taken after the task's dependency wait succeeded,
- * end is taken before its trigger. */
+/* One record per executed task (trace mode).  Tickets (trace = 1) come from
+ * one global atomic counter: start is taken after the task's dependency wait
+ * succeeded, end is taken before its trigger.  In the timing trace (trace =
+ * 2) the two ticket fields hold clocks instead: t_start the clock at task
+ * entry (its worker done with the previous task), t_end the clock when the
+ * dependency wait began (the pre-wait weight loads issued). */
 typedef struct {
   int32_t task;     /* task id (BFS order) */
   int16_t worker;   /* worker (workgroup) index; -1 in launch-per-task mode */
   int16_t xcc;      /* hardware XCC (chiplet) id the task ran on */
-  uint32_t t_start; /* global ticket at start */
-  uint32_t t_end;   /* global ticket at end (before the trigger) */
+  uint32_t t_start; /* global ticket at start (timing trace: clock at task entry) */
+  uint32_t t_end;   /* global ticket at end, before the trigger (timing trace: clock when the wait began) */
   uint32_t dep_seen;/* dependency counter value observed when the wait ended */
   uint32_t step;    /* step epoch */
   uint32_t clk_start, clk_end; /* low 32 bits of the 100 MHz device wall clock */
