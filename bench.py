@@ -349,10 +349,15 @@ def main():
             timeline.to_perfetto(recs, tasks, args.timeline_json)
         split = timeline.layer_split(recs, tasks)
         per_op = timeline.attribute(recs, tasks)
+        phases = timeline.task_phases(recs, tasks)
+        crit = timeline.op_phases(recs, tasks)
         tr.close()
         attribution = {
             "layer_split": split,
             "per_operator": {k: v for k, v in per_op.items()},
+            "task_phases": {k: {kk: (int(vv) if kk == "tasks" else float(vv)) for kk, vv in v.items()}
+                            for k, v in phases.items()},
+            "layer_critical_path_us": crit,
             "buckets": timeline.buckets(med, lpt["median_ms_per_step"] if lpt else med,
                                         lpt["graph_median_ms_per_step"] if lpt else None,
                                         bytes_mean, activation_bytes(sess), stream_gbs, HBM_PEAK_GBS, split)}

@@ -122,6 +122,72 @@ def layer_split(recs: np.ndarray, tasks: np.ndarray) -> Dict[str, float]:
             "layer_median_run_us": round(float(np.median(runs)), 2) if runs else 0.0}
 
 
+def task_phases(recs: np.ndarray, tasks: np.ndarray) -> Dict[str, dict]:
+    """Timing-trace records only (trace = 2, whose ticket fields hold the
+    clocks of task entry and of the start of the dependency wait).  Per
+    operator kind, the mean per task of four consecutive intervals on its
+    worker: ``post`` (the worker's previous trigger -> this task's entry: the
+    rest of the previous task after its trigger, its epilogue, and the next
+    descriptor), ``issue`` (entry -> wait begins: pre-wait loads issued),
+    ``wait`` (-> dependency met) and ``run`` (-> trigger).  ``_per_worker``
+    holds each interval summed over a worker's tasks, averaged over workers;
+    their sum is the mean over workers of the first entry -> last trigger."""
+    kinds = _kinds(tasks)
+    n = len(recs)
+    allc = unwrap(np.concatenate([recs["t_start"], recs["t_end"], recs["clk_start"], recs["clk_end"]]))
+    ent, wb, dm, tr = (allc[i * n:(i + 1) * n].astype(np.float64) * TICK_US for i in range(4))
+    sums: Dict[str, np.ndarray] = defaultdict(lambda: np.zeros(5))
+    by_worker = defaultdict(list)
+    for i, r in enumerate(recs):
+        by_worker[int(r["worker"])].append(i)
+    for idx in by_worker.values():
+        idx.sort(key=lambda i: ent[i])
+        prev = ent[idx[0]]
+        for i in idx:
+            a = sums[kinds[int(recs[i]["task"])]]
+            a += (1.0, ent[i] - prev, wb[i] - ent[i], dm[i] - wb[i], tr[i] - dm[i])
+            prev = tr[i]
+    out: Dict[str, dict] = {}
+    tot = np.zeros(4)
+    for k, a in sums.items():
+        out[k] = {"tasks": int(a[0]), "post_us": round(a[1] / a[0], 3), "issue_us": round(a[2] / a[0], 3),
+                  "wait_us": round(a[3] / a[0], 3), "run_us": round(a[4] / a[0], 3)}
+        tot += a[1:]
+    nw = max(len(by_worker), 1)
+    out["_per_worker"] = {"tasks": n // nw, "post_us": round(tot[0] / nw, 3), "issue_us": round(tot[1] / nw, 3),
+                          "wait_us": round(tot[2] / nw, 3), "run_us": round(tot[3] / nw, 3)}
+    return out
+
+
+def op_phases(recs: np.ndarray, tasks: np.ndarray) -> Dict[str, float]:
+    """Critical path of a layer, per operator kind: the median over layers of
+    the time from the previous operator's last trigger to this operator's last
+    trigger, the operators of a layer taken in the order of their first
+    trigger (the first operator of a layer counts from the previous layer's
+    last trigger; the first layer is skipped)."""
+    kinds = _kinds(tasks)
+    _, t1 = _times_us(recs)
+    last = defaultdict(lambda: -np.inf)
+    first = defaultdict(lambda: np.inf)
+    for i, r in enumerate(recs):
+        t = int(r["task"])
+        key = (int(tasks[t, 1]), kinds[t])
+        if key[0] < 0:
+            continue
+        last[key] = max(last[key], t1[i])
+        first[key] = min(first[key], t1[i])
+    layers = sorted({l for l, _ in last})
+    ph: Dict[str, list] = defaultdict(list)
+    prev_end = None
+    for l in layers:
+        ops = sorted([k for (ll, k) in last if ll == l], key=lambda k: first[(l, k)])
+        for k in ops:
+            if prev_end is not None:
+                ph[k].append(last[(l, k)] - prev_end)
+            prev_end = last[(l, k)]
+    return {k: round(float(np.median(v)), 2) for k, v in ph.items()}
+
+
 def buckets(t_persistent_ms: float, t_lpt_ms: float, t_graph_ms: Optional[float], alg_bytes: float,
             act_bytes: float, stream_gbs: Optional[float], peak_gbs: float = 8000.0,
             split: Optional[Dict[str, float]] = None) -> Dict[str, dict]:

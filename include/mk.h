@@ -178,28 +178,44 @@ typedef struct {
 } mk_stats;
 
 /* Compile the task graph for a model shape, batch and KV capacity (host only;
- * no device work).  *out receives a new graph, freed by mk_destroy_graph.
- * Errors: MK_ERR_ARG, MK_ERR_SHAPE. */
+ * no device work): tiling, event fusion, normalisation to at most one
+ * dependency and one trigger event per task, BFS linearisation, assignment to
+ * workers (review page of arXiv 2512.22219, section 2.4; the compile half of
+ * the survey page's compile-and-run pipeline, section 3.1).  *out receives a
+ * new graph, freed by mk_destroy_graph.  Errors: MK_ERR_ARG, MK_ERR_SHAPE. */
 mk_status mk_build_graph(const mk_model_shape* shape, int32_t batch, int32_t max_ctx, const mk_build_opts* opts,
                          mk_graph** out);
 
 /* Bytes of caller-allocated device memory the graph needs:
  *   arena   - packed weights and the read-only task tables (256 B aligned)
  *   scratch - event counters, status words and inter-task activations
- *   trace   - trace records (0 unless opts.trace) */
+ *   trace   - trace records (0 unless opts.trace)
+ * The pages' runtime keeps the task graph and the tensors between tasks in
+ * device memory for the one resident kernel (survey page on MPK, section 3:
+ * a runtime that launches and drives the compiled megakernel); here the
+ * caller allocates that memory.  Pure query: no device work.
+ * Errors: MK_ERR_ARG (null argument). */
 mk_status mk_workspace_size(const mk_graph* g, size_t* arena_bytes, size_t* scratch_bytes, size_t* trace_bytes);
 
 /* Repack the logical tensors into the arena in per-task order, upload the
  * task tables, and clear the scratch.  Asynchronous on `stream` (a
  * hipStream_t; NULL = default stream); host tensors are staged synchronously.
- * Every tensor of the shape must be present exactly once.
+ * Every tensor of the shape must be present exactly once.  This is the step
+ * before the timed decode in the pages' demo, where the model is built and
+ * its weights placed once and the decode is then a single call (survey page
+ * on MPK, section 5.3).  The tensors stay owned by the caller and may be freed
+ * after the stream is synchronised.
  * Errors: MK_ERR_ARG (missing/duplicate/misshapen tensor), MK_ERR_HIP. */
 mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void* d_arena, void* d_scratch,
                           void* d_trace, void* stream);
 
 /* Run one decode step: tokens d_tokens[B] (int32) at positions d_positions[B]
  * (int32, 0 <= pos < capacity), reading/writing the KV cache, and writing
- * fp32 logits d_logits[B][V].  Asynchronous on `stream`.
+ * fp32 logits d_logits[B][V].  Asynchronous on `stream`.  In persistent mode
+ * this is the single launch per step of the pages' megakernel timeline (survey
+ * page on MPK, section 3.2: one launch, one resident kernel, a dispatch-only
+ * scheduler beside it); in launch-per-task mode it is that section's baseline
+ * of one launch per operator range.
  * Errors: MK_ERR_STATE (weights not loaded, or a previous step failed and was
  * not cleared by mk_check), MK_ERR_ARG, MK_ERR_HIP, MK_ERR_NOT_RESIDENT. */
 mk_status mk_decode_step(mk_graph* g, const int32_t* d_tokens, const int32_t* d_positions, const mk_kv_cache* kv,
@@ -264,16 +280,26 @@ mk_status mk_capture_lpt_graph(mk_graph* g, const int32_t* d_tokens, const int32
 mk_status mk_lpt_graph_launch(mk_lpt_graph* lg, void* stream);
 void mk_lpt_graph_destroy(mk_lpt_graph* lg);
 
-/* Switch the execution mode of a loaded graph (same tables and arena). */
+/* Switch the execution mode of a loaded graph (same tables and arena):
+ * MK_PERSISTENT or MK_LAUNCH_PER_TASK (per_task_launch = 1: one launch per
+ * task), the two timelines of the survey page on MPK, section 3.2.
+ * Errors: MK_ERR_ARG (null graph, unknown mode). */
 mk_status mk_set_mode(mk_graph* g, int32_t mode, int32_t per_task_launch);
 
 /* After the caller synchronised the stream: read the device status word.
- * MK_OK, or MK_ERR_TIMEOUT (watchdog fired; the details are in the message),
- * after which the event state is reset so that the next step can run. */
+ * MK_OK, MK_ERR_ARG (a position outside the cache or a page-table entry
+ * outside the pool was clamped and reported), or MK_ERR_TIMEOUT (watchdog
+ * fired; the task, event and counter values are in the message), after which
+ * the event state is reset so that the next step can run.  The pages' runtime
+ * has no such check (a stuck event there hangs the kernel); the bounded waits
+ * behind it are this design's addition. */
 mk_status mk_check(mk_graph* g);
 
 /* After sync: copy the trace of the last step (up to cap records) to host
- * memory; *n receives the number of records written by the device. */
+ * memory; *n receives the number of records written by the device.  The
+ * counterpart of the pages' profiling trace (survey page on MPK, section 7.2:
+ * the profiling flag writes a per-task timeline).  Errors: MK_ERR_ARG,
+ * MK_ERR_STATE (graph built without trace). */
 mk_status mk_read_trace(mk_graph* g, mk_trace_rec* host_buf, int64_t cap, int64_t* n);
 
 /* After sync: verify a trace against the graph: every task exactly once, no
@@ -297,20 +323,29 @@ mk_status mk_check_trace(const mk_graph* g, const mk_trace_rec* recs, int64_t n,
 mk_status mk_read_routing(mk_graph* g, int32_t step, int32_t* experts, float* weights, float* router_logits,
                           int64_t cap);
 
-/* After sync: host copy of the per-event counter totals (events entries). */
+/* After sync: host copy of the per-event counter totals (events entries),
+ * the counters of the event protocol (review page of arXiv 2512.22219, section
+ * 2.4: a task waits on one event counter and increments one).  With
+ * mk_check_trace, every counter must equal need x steps.  Errors: MK_ERR_ARG. */
 mk_status mk_read_counters(mk_graph* g, uint32_t* host_counters, int64_t cap);
 
 /* Execute the graph's protocol on the host with `threads` threads standing in
  * for the workers and no-op task bodies, writing a trace (recs, cap >= tasks)
- * for mk_check_trace.  `fault` plants a protocol fault for checker tests:
+ * for mk_check_trace (the event protocol of the review page of arXiv
+ * 2512.22219, section 2.4, run without a GPU).  `fault` plants a protocol fault for checker tests:
  * 0 none, 1 drop one trigger (expect MK_ERR_TIMEOUT), 2 duplicate one trigger,
  * 3 start one task without waiting.  Host only, no device. */
 mk_status mk_simulate(const mk_graph* g, int32_t threads, int32_t steps, int32_t fault, int32_t timeout_ms,
                       mk_trace_rec* recs, int64_t cap, int64_t* n, uint32_t* counters);
 
+/* Task, event, empty-task and per-worker counts and the workspace sizes of a
+ * compiled graph (the "deep, not wide" shape the review page of arXiv
+ * 2512.22219 discusses in its attack notes).  Errors: MK_ERR_ARG. */
 mk_status mk_graph_stats(const mk_graph* g, mk_stats* out);
 
-/* Write the graph (tasks, events, worker lists) as JSON. */
+/* Write the graph (tasks, events, worker lists) as JSON, the counterpart of
+ * the task-graph file the pages' profiling run writes (survey page on MPK,
+ * section 7.2).  Host only.  Errors: MK_ERR_ARG (null graph or path). */
 mk_status mk_dump_graph(const mk_graph* g, const char* json_path);
 
 /* Host copies of the graph tables for inspection and tests.
@@ -326,7 +361,11 @@ mk_status mk_get_worker_lists(const mk_graph* g, int32_t* offsets, int32_t* ids,
  * edge preservation).  *n receives the count; pass rows = NULL to query. */
 mk_status mk_get_raw_edges(const mk_graph* g, int32_t* rows, int64_t cap, int64_t* n);
 
+/* Free a graph and its internal stream (the caller's device memory is not
+ * touched).  NULL is accepted. */
 void mk_destroy_graph(mk_graph* g);
+/* Message of the calling thread's last failed call ("" if none); valid until
+ * that thread's next call. */
 const char* mk_last_error(void);
 
 /* Measurement helper: read `bytes` bytes of device memory once (16-byte

@@ -94,3 +94,45 @@ def test_bucket_arithmetic():
     assert b["iii_prefetch_latency"]["layer_hops_and_tails_us"] == pytest.approx(34.0)
     assert b["v_l2_activation_reuse"]["bound_share_of_step"] == pytest.approx(0.003)
     assert b["ii_onchip_staging"]["ms"] is None
+
+
+def _timing_records(rows):
+    """rows: (task, worker, entry, wait_begin, dep_met, trigger) in ticks."""
+    recs = np.zeros(len(rows), dtype=mk.TRACE_DTYPE)
+    for i, (t, w, e, wb, d, tr) in enumerate(rows):
+        recs[i]["task"], recs[i]["worker"] = t, w
+        recs[i]["t_start"], recs[i]["t_end"] = e % (1 << 32), wb % (1 << 32)
+        recs[i]["clk_start"], recs[i]["clk_end"] = d % (1 << 32), tr % (1 << 32)
+    return recs
+
+
+# the same six tasks with entry and wait-begin clocks (timing trace)
+TROWS = [(0, 0, BASE - 20, BASE - 10, BASE + 0, BASE + 100), (1, 1, BASE - 20, BASE + 5, BASE + 10, BASE + 90),
+         (2, 1, BASE + 110, BASE + 120, BASE + 150, BASE + 300), (3, 0, BASE + 120, BASE + 200, BASE + 320, BASE + 400),
+         (4, 1, BASE + 310, BASE + 330, BASE + 450, BASE + 600), (5, 0, BASE + 420, BASE + 430, BASE + 650, BASE + 700)]
+
+
+def test_task_phases_partition_each_workers_time():
+    recs = _timing_records(TROWS)
+    ph = timeline.task_phases(recs, TASKS)
+    # worker 0: tasks 0, 3, 5 -> post 0 + 20 + 20, issue 10 + 80 + 10, wait 10 + 120 + 220, run 100 + 80 + 50
+    # worker 1: tasks 1, 2, 4 -> post 0 + 20 + 10, issue 25 + 10 + 20, wait 5 + 30 + 120, run 80 + 150 + 150
+    pw = ph["_per_worker"]
+    assert pw["post_us"] == pytest.approx((40 + 30) / 2 * timeline.TICK_US)
+    assert pw["issue_us"] == pytest.approx((100 + 55) / 2 * timeline.TICK_US)
+    assert pw["wait_us"] == pytest.approx((350 + 155) / 2 * timeline.TICK_US)
+    assert pw["run_us"] == pytest.approx((230 + 380) / 2 * timeline.TICK_US)
+    # the four intervals add up to first entry -> last trigger per worker (720 and 620 ticks)
+    assert sum(pw[k] for k in ("post_us", "issue_us", "wait_us", "run_us")) == pytest.approx(670 * timeline.TICK_US)
+    assert ph["oproj"]["tasks"] == 2
+    assert ph["oproj"]["run_us"] == pytest.approx((80 + 50) / 2 * timeline.TICK_US)
+    assert ph["attn"]["wait_us"] == pytest.approx(30 * timeline.TICK_US)
+
+
+def test_op_phases_follow_the_last_triggers():
+    recs = _timing_records(TROWS)
+    ph = timeline.op_phases(recs, TASKS)
+    # layer 0: qkv ends 100, attn 300, oproj 400; layer 1: qkv ends 600, oproj 700
+    assert ph["attn"] == pytest.approx(2.0)
+    assert ph["oproj"] == pytest.approx(np.median([1.0, 1.0]))
+    assert ph["qkv"] == pytest.approx(2.0)  # 400 -> 600 (layer 0's qkv has no predecessor)
