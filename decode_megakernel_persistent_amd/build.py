@@ -83,5 +83,16 @@ def build_tsan(verbose: bool = False) -> str:
     return exe
 
 
+def build_asan(verbose: bool = False) -> str:
+    """The same host driver built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (graph compiler, simulator, trace checker)."""
+    os.makedirs(BUILD, exist_ok=True)
+    exe = os.path.join(BUILD, "mk_sim_asan")
+    srcs = [os.path.join(CSRC, s) for s in HOST_SRCS] + [os.path.join(CSRC, "sim_main.cpp")]
+    _run(["g++", "-O1", "-g", "-std=c++17", "-pthread", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+          "-fno-omit-frame-pointer", "-I", INCLUDE, "-I", CSRC, *srcs, "-o", exe], verbose)
+    return exe
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv, tsan="--tsan" in sys.argv))
