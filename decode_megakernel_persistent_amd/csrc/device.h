@@ -836,90 +836,86 @@ DEV void gemv_valu_any(Ctx& c, const OpDesc& op) {
 //   weights: 1 KB fragments, fragment (group g of 16 rows, k-block kb of 32
 //     columns) at ((g * K/32 + kb) * 64 + lane) * 16 bytes, lane l holding
 //     row l%16, columns 8*(l/16) .. +8 (laid out at load time);
-//   inputs: staged per chunk of KC columns as bf16 fragments in LDS, fragment
-//     kb at kb * 1 KB, lane l holding sequence l%16, columns 8*(l/16) .. +8;
-//     each value x is split as hi = bf16(x), lo = bf16(x - hi) and both
-//     parts are multiplied (two MFMAs per weight fragment), so the input
-//     keeps about 16 significant bits instead of bf16's 8 (a plain bf16 input
-//     cost ~2% logits error over 36 layers at batch 16).
+//   inputs: staged per chunk of KC columns in LDS as bf16 rows, sequence b
+//     at b * kMfmaRS elements (row stride padded by 8 so that the 16 lanes of
+//     a fragment read fall in distinct banks); the input fragment of k-block
+//     kb is read from there, lane l holding sequence l%16, columns
+//     kb*32 + 8*(l/16) .. +8.  Each value x is split as hi = bf16(x),
+//     lo = bf16(x - hi) and both parts are multiplied (two MFMAs per weight
+//     fragment), so the input keeps about 16 significant bits instead of
+//     bf16's 8 (a plain bf16 input cost ~2% logits error over 36 layers at
+//     batch 16).
 // Work items are (row group, K part) pairs: tiles with fewer than eight row
 // groups split K across wavefronts (parts interleaved by k-block) and sum the
 // parts through LDS.  Each wavefront streams its items' fragments through a
 // ring of kMfmaDepth loads; every (chunk, item) segment is padded to whole
 // ring turns so that ring slots stay compile-time indices.
-constexpr int kMfmaKC = 1536;     // input columns staged per chunk (2 x 48 KB of bf16 fragments)
+constexpr int kMfmaKC = 1536;     // input columns staged per chunk
+constexpr int kMfmaRS = kMfmaKC + 8;                // staged row stride (bf16 elements)
+constexpr int kMfmaXBytes = 16 * kMfmaRS * 2;       // one staged part (hi or lo), 16 sequences
 constexpr int kMfmaDepth = 8;     // weight fragments in flight per wavefront
 constexpr int kMfmaMaxItems = 4;  // items per wavefront (row groups per tile <= 32)
 constexpr int kMfmaVariant = 16;  // kernel template value of the MFMA variant
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+static_assert(NWAVE == 8, "the MFMA stager gives wavefront w sequences w and w + 8");
+static_assert(kMfmaXBytes % 16 == 0, "staged parts stay 16-byte aligned");
 
-DEV u32 pack_bf16x2(float lo, float hi) { return (u32)f2bf(lo) | ((u32)f2bf(hi) << 16); }
-
-// Stage input columns [c0, c0 + 32*KBc) of every sequence as bf16 fragments
-// (x * g for normalising ops); ss accumulates this thread's sum of squares
-// of its sequence (tid % 16).  Slot s = tid + NT*i covers fragment kb = s/64,
-// lane (s % 64) = sequence s%16, column block (s/16)%4: one 16-byte store.
-DEV void mfma_stage(Ctx& c, const OpDesc& op, int tid, int c0, int KBc, char* xf, char* xl, float& ss) {
+// Stage input columns [c0, c0 + ncols) of every sequence (x * g for
+// normalising ops) as bf16 hi and lo rows.  Wavefront w stages sequences w
+// and w + 8 (rows past the batch are written as zeros): lane l reads words
+// c0 + l + 64 i of both sequences, so every load instruction covers 64
+// consecutive tagged words (512 bytes, whole cache lines), and kStageMfma
+// columns of both sequences (with their gains) are in flight per lane before
+// the first tag check.  ss[h] accumulates the sum of squares of the lane's
+// values of sequence w + 8 h.
+constexpr int kStageMfma = 8;  // columns per lane in flight (x 2 sequences)
+DEV void mfma_stage(Ctx& c, const OpDesc& op, int tid, int c0, int ncols, uint16_t* xh, uint16_t* xo, float (&ss)[2]) {
   const StepArgs& a = *c.a;
   const int B = a.geom->B, K = op.K;
-  const int b = tid & 15;
-  const int nslot = KBc * 64;
-  constexpr int BATCH = 2;  // slots (8 words each) in flight per thread
-  for (int i0 = 0; i0 < (kMfmaKC / 32) * 64 / NT; i0 += BATCH) {
-    if (i0 * NT >= nslot) break;
-    u64 w[BATCH][8];
-    bool ok[BATCH];
-    int kcol[BATCH];
+  const int wave = tid >> 6, lane = tid & 63;
+  bool live[2];
+  const u64* src[2];
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) {
-      const int s = tid + NT * (i0 + i);
-      const int kb = s >> 6, m = (s >> 4) & 3;
-      kcol[i] = c0 + kb * 32 + m * 8;
-      ok[i] = s < nslot && b < B;
-      const u64* src = op.in + (size_t)(b < B ? b : 0) * K + (ok[i] ? kcol[i] : 0);
+  for (int h = 0; h < 2; ++h) {
+    const int b = wave + 8 * h;
+    live[h] = b < B;
+    src[h] = op.in + (size_t)(live[h] ? b : 0) * K + c0;
+  }
+  for (int j0 = 0; j0 * 64 < ncols; j0 += kStageMfma) {
+    u64 w[2][kStageMfma];
+    float g[kStageMfma];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[i][e] = ld_raw(src + e);
+    for (int i = 0; i < kStageMfma; ++i) {
+      const int col = min(lane + 64 * (j0 + i), ncols - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) w[h][i] = ld_raw(src[h] + col);
+      g[i] = op.norm_in ? ldg(op.g + c0 + col) : 1.0f;
     }
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) {
-      const int s = tid + NT * (i0 + i);
-      if (s < nslot) {
-        u32x4 o = {0u, 0u, 0u, 0u}, ol = {0u, 0u, 0u, 0u};
-        if (ok[i]) {
-          const u64* src = op.in + (size_t)b * K + kcol[i];
-          float v[8];
+    for (int i = 0; i < kStageMfma; ++i) {
+      const int col = lane + 64 * (j0 + i);
+      if (col < ncols) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            v[e] = fix_t(w[i][e], src + e, a);
-            ss += v[e] * v[e];
+        for (int h = 0; h < 2; ++h) {
+          uint16_t hi = 0, lo = 0;
+          if (live[h]) {
+            const float v = fix_t(w[h][i], src[h] + col, a);
+            ss[h] += v * v;
+            const float x = v * g[i];
+            hi = f2bf(x);
+            lo = f2bf(x - bf2f(hi));
           }
-          if (op.norm_in) {
-            const f32x4 g0 = *(const f32x4*)(op.g + kcol[i]);
-            const f32x4 g1 = *(const f32x4*)(op.g + kcol[i] + 4);
-            v[0] *= g0.x; v[1] *= g0.y; v[2] *= g0.z; v[3] *= g0.w;
-            v[4] *= g1.x; v[5] *= g1.y; v[6] *= g1.z; v[7] *= g1.w;
-          }
-          float lo[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf2f(f2bf(v[e]));
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          o.z = pack_bf16x2(v[4], v[5]);
-          o.w = pack_bf16x2(v[6], v[7]);
-          ol.x = pack_bf16x2(lo[0], lo[1]);
-          ol.y = pack_bf16x2(lo[2], lo[3]);
-          ol.z = pack_bf16x2(lo[4], lo[5]);
-          ol.w = pack_bf16x2(lo[6], lo[7]);
+          const int e = (wave + 8 * h) * kMfmaRS + col;
+          xh[e] = hi;
+          xo[e] = lo;
         }
-        *(u32x4*)(xf + (size_t)s * 16) = o;
-        *(u32x4*)(xl + (size_t)s * 16) = ol;
       }
     }
   }
 }
 
 // LDS locations of the MFMA path's per-row results [B][NR] and norm scales [16].
-DEV const float* mfma_rows(const Ctx& c) { return (const float*)(c.lds + 2 * (kMfmaKC / 32 * 1024)); }
+DEV const float* mfma_rows(const Ctx& c) { return (const float*)(c.lds + 2 * kMfmaXBytes); }
 DEV const float* mfma_scales(const Ctx& c) { return mfma_rows(c) + kRowResultFloats + NWAVE * 256 + 16 * NWAVE; }
 
 DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
@@ -967,25 +963,27 @@ DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
   for (int d = 0; d < DEPTH; ++d) buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
 
   wait_dep(c);
-  char* xf = c.lds;                                  // [KBc][64 lanes][16 B], hi parts
-  char* xl = xf + kMfmaKC / 32 * 1024;               // lo parts
-  float* rsl = (float*)(xl + kMfmaKC / 32 * 1024);   // [B][NR]
+  uint16_t* xh = (uint16_t*)c.lds;                   // [16][kMfmaRS] bf16, hi parts
+  uint16_t* xo = xh + 16 * kMfmaRS;                   // lo parts
+  float* rsl = (float*)(c.lds + 2 * kMfmaXBytes);    // [B][NR]
   float* part = rsl + kRowResultFloats;              // [item][16 seq][16 rows]
   float* red = part + NWAVE * 256;                   // [16 seq][NWAVE]
   float* rn = red + 16 * NWAVE;                      // [16]
   const u64 res0 = gemv_residual_prefetch(c, op, B);
-  float ss = 0.f;
-  mfma_stage(c, op, tid, 0, min(KBc, KB), xf, xl, ss);
+  float ss[2] = {0.f, 0.f};
+  mfma_stage(c, op, tid, 0, min(KBc, KB) * 32, xh, xo, ss);
   __syncthreads();
 
   f32x4 acc[kMfmaMaxItems];
 #pragma unroll
   for (int i = 0; i < kMfmaMaxItems; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // input fragment of this lane: sequence lane % 16, columns 8 * (lane / 16) .. +8 of a k-block
+  const int xrow = (lane & 15) * kMfmaRS + (lane >> 4) * 8;
   for (int cc = 0; cc < nchunks; ++cc) {
     const int kbc = min(KBc, KB - cc * KBc);  // k-blocks in this chunk
     if (cc > 0) {
       __syncthreads();
-      mfma_stage(c, op, tid, cc * KC, kbc, xf, xl, ss);
+      mfma_stage(c, op, tid, cc * KC, kbc * 32, xh, xo, ss);
       __syncthreads();
     }
 #pragma unroll
@@ -997,8 +995,8 @@ DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
           for (int d = 0; d < DEPTH; ++d) {
             const int j = j0 + d, kbl = q + j * kparts;
             if (j < NJ && kbl < kbc) {
-              const u32x4 xv = *(const u32x4*)(xf + (size_t)kbl * 1024 + lane * 16);
-              const u32x4 xw = *(const u32x4*)(xl + (size_t)kbl * 1024 + lane * 16);
+              const u32x4 xv = *(const u32x4*)(xh + xrow + kbl * 32);
+              const u32x4 xw = *(const u32x4*)(xo + xrow + kbl * 32);
               const bf16x8 wv = __builtin_bit_cast(bf16x8, buf[d]);
               acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, __builtin_bit_cast(bf16x8, xv), acc[it], 0, 0, 0);
               acc[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, __builtin_bit_cast(bf16x8, xw), acc[it], 0, 0, 0);
@@ -1024,10 +1022,9 @@ DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[wave * 256 + n * 16 + r4 + r] = acc[0][r];
   }
-  // sum of squares per sequence: lanes l, l^16, l^32, l^48 share a sequence
-  ss += __shfl_xor(ss, 16);
-  ss += __shfl_xor(ss, 32);
-  if (lane < 16) red[lane * NWAVE + wave] = ss;
+  // sum of squares per sequence: wavefront w staged sequences w and w + 8
+  const float s0 = wave_sum(ss[0]), s1 = wave_sum(ss[1]);
+  if (lane < 16) red[lane * NWAVE + wave] = lane == wave ? s0 : (lane == wave + 8 ? s1 : 0.f);
   __syncthreads();
   if (kparts > 1) {
     for (int j = tid; j < B * NR; j += NT) {
