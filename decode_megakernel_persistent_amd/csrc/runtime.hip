@@ -266,7 +266,10 @@ __global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) {
         c.lds = nullptr;
         c.flags = flags;
         c.pos = nullptr;
-        if (threadIdx.x == 0) flags[5] = 0;
+        if (threadIdx.x == 0) {
+          flags[5] = 0;
+          if (a.trace_on == 2) flags[kFlagEntryClock] = (int)(u32)wall_clock64();
+        }
         wait_dep(c);
         if (flags[0]) return;
         route_wave(as, a.ops[c.t.op], threadIdx.x);
