@@ -1645,17 +1645,116 @@ DEV int moe_load_tokens(Ctx& c, const u64* table, int e, int* s_tok, int tid) {
   return n;
 }
 
+// The expert slots stream their items' weights through a ring whose slot of
+// every load is a compile-time index: an item is NL loads per lane in a fixed
+// order, NL a multiple of the ring depth, so the load DEPTH ahead of load l
+// of an item is load l + DEPTH of the same item or load l + DEPTH - NL of the
+// next one.  Items past the slot's share load out of range (zeros).
+template <int NL>
+struct MoeRing {
+  static constexpr int DEPTH = NL % 8 == 0 ? 8 : 4;
+  static_assert(NL % DEPTH == 0, "items are whole ring turns");
+};
+
 // Expert gate-up slot: for each item (expert e, 16-row unit u) and each token
 // of e: act[slot][16u + r] = silu(gate_r . h) * (up_r . h).  Weights of one
 // unit: 16 gate rows then 16 up rows, rows of H contiguous bf16.  Wavefront w
 // computes outputs r = w and w + 8 (gate and up rows in the same wavefront);
-// an 8-load ring streams (item, output, gate/up, chunk) in order, 16 loads per
-// item per lane.
+// an item is NL = 4 * NCH loads per lane in the order (output, gate/up,
+// 1 KB chunk of the row), NCH = H / 512 chunks per row.
+template <int NCH>
+DEV void moe_gu_items(Ctx& c, const OpDesc& op, const float* xs, const int* s_act, int* s_tok, int i0, int i1) {
+  const StepArgs& a = *c.a;
+  const Geom& G = *a.geom;
+  const int K = G.topk, Ie = G.Ie, H = op.K;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  const int U = Ie / 16;
+  constexpr int NL = 4 * NCH, DEPTH = MoeRing<NL>::DEPTH;
+  // weights of every expert: [E][2*Ie][H]; unit u of e starts at row e*2*Ie + 32u
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)op.w, (short)0, (int)((u32)G.E * 2u * (u32)Ie * (u32)H * 2u), 0x00020000);
+  auto rowbase = [&](int it) -> int {  // this wavefront's first row of item it (-1 past the share)
+    if (it >= i1) return -1;
+    const int e = s_act[it / U];
+    return e * 2 * Ie + (it - (it / U) * U) * 32 + wave;
+  };
+  auto off = [&](int rb, int l) -> u32 {
+    const int o = l / (2 * NCH), gu = (l / NCH) & 1, q = l % NCH;
+    const int cc = q * 64 + lane;
+    if (rb < 0 || cc * 8 >= H) return OOB;
+    return (u32)(((rb + gu * 16 + 8 * o) * H + cc * 8) * 2);
+  };
+  int rb = rowbase(i0), rb_next = rowbase(i0 + 1);
+  u32x4 buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(rb, d), 0, AUX_NT);
+  int cur_e = -1, ntok = 0;
+  int xoff[8], slot[8];
+  const u64* table = op.aux + route_tb(G);
+  for (int it = i0; it < i1; ++it) {
+    const int e = s_act[it / U], u = it - (it / U) * U;
+    if (e != cur_e) {
+      ntok = moe_load_tokens(c, table, e, s_tok, tid);
+      // uniform per workgroup: kept in scalar registers
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        slot[t] = __builtin_amdgcn_readfirstlane(s_tok[t < ntok ? t : 0]);
+        xoff[t] = __builtin_amdgcn_readfirstlane((slot[t] / K) * H);  // the token's sequence row of xs
+      }
+      cur_e = e;
+    }
+    float acc[2][2][8];  // [output][gate/up][token]
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[o][g2][t] = 0.f;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int o = l / (2 * NCH), gu = (l / NCH) & 1, q = l % NCH, d = l % DEPTH;
+      const int cc = q * 64 + lane;
+      const u32x4 wv = buf[d];
+      if (cc * 8 < H) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if (t < ntok) {
+            const f32x4 x0 = *(const f32x4*)(xs + xoff[t] + cc * 8);
+            const f32x4 x1 = *(const f32x4*)(xs + xoff[t] + cc * 8 + 4);
+            float sacc = bf_lo(wv.x) * x0.x;
+            sacc = fmaf(bf_hi(wv.x), x0.y, sacc);
+            sacc = fmaf(bf_lo(wv.y), x0.z, sacc);
+            sacc = fmaf(bf_hi(wv.y), x0.w, sacc);
+            sacc = fmaf(bf_lo(wv.z), x1.x, sacc);
+            sacc = fmaf(bf_hi(wv.z), x1.y, sacc);
+            sacc = fmaf(bf_lo(wv.w), x1.z, sacc);
+            sacc = fmaf(bf_hi(wv.w), x1.w, sacc);
+            acc[o][gu][t] += sacc;
+          }
+        }
+      }
+      buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, l + DEPTH < NL ? off(rb, l + DEPTH) : off(rb_next, l + DEPTH - NL),
+                                                     0, AUX_NT);
+    }
+    rb = rb_next;
+    rb_next = rowbase(it + 2);
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < ntok) {
+          const float gsum = wave_sum(acc[o][0][t]), usum = wave_sum(acc[o][1][t]);
+          if (lane == 0) st_t(op.out + (size_t)slot[t] * Ie + u * 16 + wave + 8 * o, silu(gsum) * usum, a.tag);
+        }
+      }
+  }
+}
+
 DEV void body_moe_gu(Ctx& c, const OpDesc& op) {
   const StepArgs& a = *c.a;
   const Geom& G = *a.geom;
-  const int B = G.B, K = G.topk, Ie = G.Ie, H = op.K;
-  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  const int Ie = G.Ie, H = op.K;
+  const int tid = task_tid();
   const int U = Ie / 16;
   float* xs = (float*)c.lds;                                   // [B][H]
   int* s_act = (int*)(c.lds + (size_t)kStageFloats * 4);       // [E]
@@ -1666,93 +1765,17 @@ DEV void body_moe_gu(Ctx& c, const OpDesc& op) {
   const int n_act = moe_load_active(c, route + route_ta(G), s_act, tid);
   const int total = n_act * U, ns = op.ntasks, s = c.t.a0;
   const int i0 = (int)((long)s * total / ns), i1 = (int)((long)(s + 1) * total / ns);
-  const int nchunk = (H / 8 + 63) / 64;  // 16-byte chunks per lane per row (H = 2048: 4)
   if (i1 <= i0) return;  // uniform across the workgroup
   moe_stage_norm(c, op, tid, xs, red);
-  // weights of every expert: [E][2*Ie][H]; unit u of e starts at row e*2*Ie + 32u
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)op.w, (short)0, (int)((u32)G.E * 2u * (u32)Ie * (u32)H * 2u), 0x00020000);
-  constexpr int DEPTH = 8;
-  const int NL = 4 * nchunk;                  // loads per item per lane (2 outputs x gate/up x chunks)
-  const int NLp = (NL + DEPTH - 1) / DEPTH * DEPTH;
-  int fi = i0, fl = 0;
-  auto fill = [&]() -> u32 {
-    u32 off = OOB;
-    if (fi < i1 && fl < NL) {
-      const int e = s_act[fi / U], u = fi - (fi / U) * U;
-      const int o = fl / (2 * nchunk), gu = (fl / nchunk) & 1, q = fl % nchunk;
-      const int row = e * 2 * Ie + u * 32 + gu * 16 + wave + 8 * o;
-      const int cc = q * 64 + lane;
-      if (cc * 8 < H) off = (u32)((row * H + cc * 8) * 2);
-    }
-    if (++fl == NLp) {
-      fl = 0;
-      ++fi;
-    }
-    return off;
-  };
-  u32x4 buf[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
-  int cur_e = -1, ntok = 0;
-  const u64* table = route + route_tb(G);
-  for (int it = i0; it < i1; ++it) {
-    const int e = s_act[it / U], u = it - (it / U) * U;
-    if (e != cur_e) {
-      ntok = moe_load_tokens(c, table, e, s_tok, tid);
-      cur_e = e;
-    }
-    float acc[2][2][8];  // [output][gate/up][token]
-#pragma unroll
-    for (int o = 0; o < 2; ++o)
-#pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[o][g2][t] = 0.f;
-    for (int l0 = 0; l0 < NLp; l0 += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int l = l0 + d;
-        if (l < NL) {
-          const int o = l / (2 * nchunk), gu = (l / nchunk) & 1, q = l % nchunk;
-          const int cc = q * 64 + lane;
-          if (cc * 8 < H) {
-            const u32x4 wv = buf[d];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              if (t < ntok) {
-                const int b = s_tok[t] / K;
-                const f32x4 x0 = *(const f32x4*)(xs + b * H + cc * 8);
-                const f32x4 x1 = *(const f32x4*)(xs + b * H + cc * 8 + 4);
-                float sacc = bf_lo(wv.x) * x0.x;
-                sacc = fmaf(bf_hi(wv.x), x0.y, sacc);
-                sacc = fmaf(bf_lo(wv.y), x0.z, sacc);
-                sacc = fmaf(bf_hi(wv.y), x0.w, sacc);
-                sacc = fmaf(bf_lo(wv.z), x1.x, sacc);
-                sacc = fmaf(bf_hi(wv.z), x1.y, sacc);
-                sacc = fmaf(bf_lo(wv.w), x1.z, sacc);
-                sacc = fmaf(bf_hi(wv.w), x1.w, sacc);
-                // o and gu are uniform: select the accumulator without dynamic indexing
-                if (o == 0 && gu == 0) acc[0][0][t] += sacc;
-                else if (o == 0) acc[0][1][t] += sacc;
-                else if (gu == 0) acc[1][0][t] += sacc;
-                else acc[1][1][t] += sacc;
-              }
-            }
-          }
-        }
-        buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
-      }
-    }
-#pragma unroll
-    for (int o = 0; o < 2; ++o)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t < ntok) {
-          const float gsum = wave_sum(acc[o][0][t]), usum = wave_sum(acc[o][1][t]);
-          if (lane == 0) st_t(op.out + (size_t)s_tok[t] * Ie + u * 16 + wave + 8 * o, silu(gsum) * usum, a.tag);
-        }
-      }
+  switch ((H / 8 + 63) / 64) {  // 1 KB chunks per row (the graph admits H <= 4096)
+    case 1: moe_gu_items<1>(c, op, xs, s_act, s_tok, i0, i1); break;
+    case 2: moe_gu_items<2>(c, op, xs, s_act, s_tok, i0, i1); break;
+    case 3: moe_gu_items<3>(c, op, xs, s_act, s_tok, i0, i1); break;
+    case 4: moe_gu_items<4>(c, op, xs, s_act, s_tok, i0, i1); break;
+    case 5: moe_gu_items<5>(c, op, xs, s_act, s_tok, i0, i1); break;
+    case 6: moe_gu_items<6>(c, op, xs, s_act, s_tok, i0, i1); break;
+    case 7: moe_gu_items<7>(c, op, xs, s_act, s_tok, i0, i1); break;
+    default: moe_gu_items<8>(c, op, xs, s_act, s_tok, i0, i1); break;
   }
 }
 

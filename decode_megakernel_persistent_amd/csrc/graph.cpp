@@ -974,8 +974,8 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   if (s.n_experts > 0 && (s.top_k <= 0 || s.top_k > s.n_experts || s.top_k > 8 || s.expert_intermediate % 16 ||
                           s.expert_intermediate <= 0 || s.n_experts > 256))
     return bad("bad expert configuration (top_k <= 8, expert_intermediate multiple of 16, <= 256 experts)");
-  if (s.n_experts > 0 && (batch > 8 || s.expert_intermediate > 1024 || s.hidden % 64))
-    return bad("routed experts support batch <= 8 and expert_intermediate <= 1024");
+  if (s.n_experts > 0 && (batch > 8 || s.expert_intermediate > 1024 || s.hidden % 64 || s.hidden > 4096))
+    return bad("routed experts support batch <= 8, expert_intermediate <= 1024 and hidden <= 4096");
   if (batch <= 0 || batch > 16) return bad("batch must be in 1..16");
   if (cap <= 0 || cap > (1 << 20)) return bad("max_ctx out of range");
   if (workers <= 0 || workers > 4096) return bad("worker count out of range");
