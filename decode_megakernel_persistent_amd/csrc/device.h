@@ -1801,21 +1801,23 @@ DEV void body_moe_down(Ctx& c, const OpDesc& op) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)op.w, (short)0, (int)((u32)G.E * (u32)H * (u32)Ie * 2u), 0x00020000);
   constexpr int DEPTH = 8;
-  const int NL = 8 * nchunk;
-  const int NLp = (NL + DEPTH - 1) / DEPTH * DEPTH;
-  int fi = i0, fl = 0;
+  const int NL = 8 * nchunk;  // loads per item per lane: 8 rows x nchunk chunks (a multiple of DEPTH)
+  auto rowbase = [&](int it) -> int {  // this wavefront's first row of item it (-1 past the share)
+    if (it >= i1) return -1;
+    const int e = s_act[it / U];
+    return e * H + (it - (it / U) * U) * 64 + wave;
+  };
+  // fill cursor: item fi (first row f_rb), row fr, chunk fq; no division per load
+  int fi = i0, fr = 0, fq = 0, f_rb = rowbase(i0);
   auto fill = [&]() -> u32 {
-    u32 off = OOB;
-    if (fi < i1 && fl < NL) {
-      const int e = s_act[fi / U], u = fi - (fi / U) * U;
-      const int r = fl / nchunk, q = fl % nchunk;
-      const int row = e * H + u * 64 + wave + 8 * r;
-      const int cc = q * 64 + lane;
-      if (cc * 8 < Ie) off = (u32)((row * Ie + cc * 8) * 2);
-    }
-    if (++fl == NLp) {
-      fl = 0;
-      ++fi;
+    const int cc = fq * 64 + lane;
+    const u32 off = (f_rb >= 0 && cc * 8 < Ie) ? (u32)(((f_rb + 8 * fr) * Ie + cc * 8) * 2) : OOB;
+    if (++fq == nchunk) {
+      fq = 0;
+      if (++fr == 8) {
+        fr = 0;
+        f_rb = rowbase(++fi);
+      }
     }
     return off;
   };
@@ -1823,6 +1825,7 @@ DEV void body_moe_down(Ctx& c, const OpDesc& op) {
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
   int cur_e = -1, ntok = 0;
+  int slot[8];  // the expert's token slots (uniform: scalar registers)
   const u64* table = route + route_tb(G);
   for (int it = i0; it < i1; ++it) {
     const int e = s_act[it / U], u = it - (it / U) * U;
@@ -1846,18 +1849,19 @@ DEV void body_moe_down(Ctx& c, const OpDesc& op) {
           xin[t * Ie + k] = fix_t(wv[i], op.in + (size_t)s_tok[t] * Ie + k, a);
         }
       }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) slot[t] = __builtin_amdgcn_readfirstlane(s_tok[t < ntok ? t : 0]);
       __syncthreads();
       cur_e = e;
     }
     float acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = 0.f;
-    for (int l0 = 0; l0 < NLp; l0 += DEPTH) {
+    int r = 0, q = 0;  // consume cursor: row, chunk
+    for (int l0 = 0; l0 < NL; l0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        const int l = l0 + d;
-        if (l < NL) {
-          const int r = l / nchunk, q = l % nchunk;
+        {
           const int cc = q * 64 + lane;
           if (cc * 8 < Ie) {
             const u32x4 wv = buf[d];
@@ -1884,10 +1888,14 @@ DEV void body_moe_down(Ctx& c, const OpDesc& op) {
             for (int t = 0; t < 8; ++t) {
               if (t < ntok) {
                 const float v = wave_sum(acc[t]);
-                if (lane == 0) st_t(op.out + (size_t)s_tok[t] * H + u * 64 + wave + 8 * r, v, a.tag);
+                if (lane == 0) st_t(op.out + (size_t)slot[t] * H + u * 64 + wave + 8 * r, v, a.tag);
               }
               acc[t] = 0.f;
             }
+          }
+          if (++q == nchunk) {
+            q = 0;
+            ++r;
           }
         }
         buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
