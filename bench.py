@@ -202,6 +202,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-only", action="store_true", help="one mode's steps only (for profilers)")
     ap.add_argument("--profile-mode", choices=["persistent", "lpt"], default="persistent")
+    ap.add_argument("--lds-ring", action="store_true",
+                    help="batch-1 GEMV tiles fed through the LDS weight ring instead of registers")
     ap.add_argument("--no-watchdog", action="store_true",
                     help="launch no dispatch wavefront (for counter runs, which serialise dispatches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -236,7 +238,7 @@ def main():
     log(f"inputs ready in {time.perf_counter() - t_setup:.1f}s")
 
     mode = mk.MK_LAUNCH_PER_TASK if args.profile_only and args.profile_mode == "lpt" else mk.MK_PERSISTENT
-    sess = mk.Session(s, B, cap, mk.make_opts(mode=mode, no_watchdog=int(args.no_watchdog)))
+    sess = mk.Session(s, B, cap, mk.make_opts(mode=mode, no_watchdog=int(args.no_watchdog), lds_ring=int(args.lds_ring)))
     sess.load(weights)
     sess.set_kv(kv_k, kv_v)
     tok_dev = torch.as_tensor(toks.T.copy(), device=sess.device)  # [ntok, B]
@@ -336,7 +338,7 @@ def main():
     attribution = None
     if args.attribution:
         # one step with the timing trace (clocks only, one record per task)
-        tr = mk.Session(s, B, cap, mk.make_opts(trace=2))
+        tr = mk.Session(s, B, cap, mk.make_opts(trace=2, lds_ring=int(args.lds_ring)))
         tr.load(weights)
         tr.set_kv(kv_k, kv_v)
         for i in range(2):
@@ -365,7 +367,7 @@ def main():
 
     paged = None
     if args.paged:
-        ps = mk.Session(s, B, cap, mk.make_opts(), page_size=args.paged, spare_pages=B, page_seed=1)
+        ps = mk.Session(s, B, cap, mk.make_opts(lds_ring=int(args.lds_ring)), page_size=args.paged, spare_pages=B, page_seed=1)
         ps.load(weights)
         ps.set_kv(kv_k, kv_v)
         t_p, _, _, _ = time_steps(ps, tok_dev, pos0, args.warmup, args.steps, False)

@@ -79,7 +79,8 @@ class mk_build_opts(ctypes.Structure):
                 ("trace", ctypes.c_int32), ("attn_chunks", ctypes.c_int32), ("gemv", ctypes.c_int32),
                 ("spin_timeout_us", ctypes.c_int32), ("no_fusion", ctypes.c_int32), ("merge_tasks", ctypes.c_int32),
                 ("no_watchdog", ctypes.c_int32), ("prefetch_loads", ctypes.c_int32),
-                ("late_trigger", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("late_trigger", ctypes.c_int32), ("lds_ring", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
 
 class mk_tensor(ctypes.Structure):
@@ -97,7 +98,7 @@ class mk_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "tasks", "empty_tasks", "events", "ops", "workers", "launches_per_step", "raw_edges", "reduced_edges",
         "max_tasks_per_worker", "weight_bytes", "arena_bytes", "scratch_bytes", "trace_bytes")] + \
-        [(n, ctypes.c_int32) for n in ("batch", "max_ctx", "attn_chunks", "gemv")]
+        [(n, ctypes.c_int32) for n in ("batch", "max_ctx", "attn_chunks", "gemv", "ring_kb", "ring_ops")]
 
 
 TRACE_DTYPE = np.dtype([("task", np.int32), ("worker", np.int16), ("xcc", np.int16), ("t_start", np.uint32),
@@ -192,12 +193,12 @@ def make_shape(s) -> mk_model_shape:
 
 def make_opts(mode=MK_PERSISTENT, per_task_launch=0, num_workers=0, trace=0, attn_chunks=0, gemv=MK_GEMV_AUTO,
               spin_timeout_us=0, no_fusion=0, merge_tasks=0, no_watchdog=0,
-              prefetch_loads=0, late_trigger=0) -> mk_build_opts:
+              prefetch_loads=0, late_trigger=0, lds_ring=0) -> mk_build_opts:
     o = mk_build_opts()
     o.mode, o.per_task_launch, o.num_workers, o.trace = mode, per_task_launch, num_workers, trace
     o.attn_chunks, o.gemv, o.spin_timeout_us, o.no_fusion = attn_chunks, gemv, spin_timeout_us, no_fusion
     o.merge_tasks, o.no_watchdog, o.prefetch_loads = merge_tasks, no_watchdog, prefetch_loads
-    o.late_trigger = late_trigger
+    o.late_trigger, o.lds_ring = late_trigger, lds_ring
     return o
 
 

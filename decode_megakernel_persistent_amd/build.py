@@ -36,7 +36,7 @@ HIP_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-pthread", "-Wall"]
 HOST_SRCS = ["graph.cpp", "sim.cpp"]
-KERNEL_VARIANTS = [1, 2, 3, 4, 16]  # VALU batches 1..4, and the MFMA variant (kMfmaVariant)
+KERNEL_VARIANTS = [1, 2, 3, 4, 16, 17]  # VALU batches 1..4, the MFMA variant (kMfmaVariant), batch 1 with the LDS ring (kRingVariant)
 
 
 def _run(cmd, verbose):

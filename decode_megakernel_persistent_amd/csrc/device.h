@@ -26,9 +26,11 @@ typedef uint32_t u32;
 typedef uint64_t u64;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = 512;       // threads per worker workgroup (8 wavefronts)
 constexpr int NWAVE = NT / 64;
+constexpr int kRingVariant = 17;  // kernel template value of the batch-1 LDS-ring variant
 constexpr u32 OOB = 0x80000000u;  // buffer offset beyond every tile: the load returns zeros
 constexpr int AUX_NT = 2;         // non-temporal hint for streamed weights
 
@@ -99,6 +101,18 @@ DEV const g_u64* gp(const u64* p) { return (const g_u64*)p; }
 DEV g_u32* gp(u32* p) { return (g_u32*)p; }
 typedef __attribute__((address_space(1))) const float g_cf32;
 DEV float ldg(const float* p) { return *(g_cf32*)p; }
+
+// Buffer resource over [p, p + bytes).  Every resource here is built from
+// per-task values, the same in every lane; readfirstlane states that to the
+// compiler, which otherwise may keep the descriptor in vector registers and
+// wrap each buffer load in a loop over distinct descriptor values.
+DEV __amdgpu_buffer_rsrc_t rsrc_u(const void* p, u32 bytes) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const u32 lo = (u32)__builtin_amdgcn_readfirstlane((int)(u32)v);
+  const u32 hi = (u32)__builtin_amdgcn_readfirstlane((int)(u32)(v >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+}
 
 // ---------------------------------------------------------------- tagged words
 DEV u64 pack(float v, u32 tag) { return ((u64)tag << 32) | (u64)__float_as_uint(v); }
@@ -187,6 +201,7 @@ DEV float wave_max(float v) {
 // seen, tickets, clocks, trigger state) and 8..44 (GEMV reduction slots).
 constexpr int kFlagEntryClock = 60;  // timing trace: clock at task entry
 constexpr int kFlagWaitClock = 61;   // timing trace: clock when the dependency wait began
+constexpr int kFlagWords = 128;      // size of the static flags block (64.. : the LDS weight ring)
 
 // ---------------------------------------------------------------- task context
 struct Ctx {
@@ -198,6 +213,7 @@ struct Ctx {
   char* lds;     // dynamic LDS (kLdsBytes)
   int* flags;    // small static LDS block: [0] abort, [1] seen, [2] start ticket, [3] start clock
   const int* pos;  // this step's positions, copied to LDS at kernel entry
+  int next;        // the worker's next task id in this step, or -1 (launch-per-task: -1)
 };
 
 // One poll of an event: lane i < kSubCounters loads sub-counter i
@@ -713,7 +729,7 @@ DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   const bool early = (op.pad & 2) != 0;  // trigger before the epilogue (tagged outputs)
   const uint16_t* Wt = op.w + (size_t)(u32)t.a3;
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, (int)((u32)NR * (u32)K * 2u), 0x00020000);
+      rsrc_u(Wt, (u32)NR * (u32)K * 2u);
 
   u32x4 buf[DEPTH][S];
   // segment (fi, fq) of the refill cursor
@@ -828,6 +844,406 @@ DEV void gemv_valu_any(Ctx& c, const OpDesc& op) {
   else gemv_valu_s<NB, kRingShallow>(c, op);
 }
 
+// ---------------------------------------------------------------- GEMV (batch 1, LDS weight ring)
+// Batch-1 tiles whose rows are whole kilobytes.  Wavefronts 4..7 are
+// loaders: they stream the tile's weights into a ring of 4 KB LDS slots with
+// LDS-DMA loads (global_load_lds_dwordx4: the data lands in LDS, no register
+// holds it in flight; one wavefront alone issues them at only ~60% of the HBM
+// rate, and the loaders also spend time on the ring's flags), and once the tile's last segment is issued they go on
+// into the next GEMV tile of the worker's list, so the compute unit keeps
+// weight bytes in flight through this tile's tail, epilogue and trigger and
+// through the next tile's dependency wait and input staging.  Wavefronts
+// 0..3 stage the input (their loads queue behind no weight loads), take ring
+// segments round-robin and leave one partial dot product per segment; the
+// epilogue sums each row's partials in a fixed order, so results do not
+// depend on timing.
+//   segment = U KB of the tile (U = Geom::ring_u: 4, 2 or 1, dividing every
+//     ring op's row bytes), i.e. part of one row;
+//   ring sequence numbers q count segments over the worker's run; segment q
+//     goes to slot q mod kRingSlots and is loaded by loader q mod 4 (the slot
+//     count is a multiple of 4, so each loader owns the slots q = j mod 4);
+//   flags[kFrFill + s] = the sequence number that last landed in slot s
+//     (published by its loader after a vmcnt wait), flags[kFrSlot + s] = the
+//     sequence number slot s may take next (a consumer sets q + kRingSlots
+//     when done with q).
+constexpr int kRingSlots = 24;     // 4 KB slots
+constexpr int kRingLoaders = 4;
+constexpr int kRingInflight = 4;   // segments in flight per loader (4 loads each at most: vmcnt <= 16);
+                                   // fewer than its slots, so landed segments wait in free slots
+                                   // instead of stalling the loader until they are consumed
+constexpr int kRingCons = NWAVE - kRingLoaders;  // consumer wavefronts
+constexpr int kRingThreads = kRingCons * 64;
+constexpr int kRingXs = 0;         // LDS byte offsets: staged input [K]
+constexpr int kRingPart = 49152;   // per-segment partial sums
+constexpr int kRingRows = 57344;   // row sums (lm_head candidates)
+constexpr int kRingBase = 61440;   // the ring
+constexpr int kRingStageCH = 24;   // input words per consumer thread in flight
+static_assert(kRingBase + kRingSlots * 4096 <= kLdsBytes, "ring fits the worker's LDS");
+static_assert(kRingSlots % kRingLoaders == 0 && kRingInflight * kRingLoaders < kRingSlots, "ring slots");
+static_assert(kRingMaxK * 4 <= kRingPart, "input staging");
+static_assert(kRingMaxSegs * 4 <= kRingRows - kRingPart && kRingMaxRows * 4 <= kRingBase - kRingRows, "LDS areas");
+// flags[] slots of the ring (the static block has kFlagWords entries)
+constexpr int kFrQi = 64;      // [kRingLoaders] loader j: next sequence number to issue
+constexpr int kFrQp = 68;      // [kRingLoaders] loader j: next sequence number to publish
+constexpr int kFrAhead = 72;   // task id the loaders ran ahead into, or -1
+constexpr int kFrAheadQ0 = 73; // its first sequence number
+constexpr int kFrGo = 74;      // dependency met (wavefront 0 -> consumers)
+constexpr int kFrStaged = 75;  // consumer wavefronts done staging
+constexpr int kFrSlot = 76;    // [kRingSlots]
+constexpr int kFrDone = 124;   // consumer wavefronts done with this tile's segments
+constexpr int kFrFill = kFrSlot + kRingSlots;  // [kRingSlots]
+static_assert(kFrFill + kRingSlots <= kFrDone && kFrDone < kFlagWords, "ring flags fit");
+
+// s_waitcnt vmcnt(N), other counters not waited on (gfx9 encoding)
+template <int N>
+DEV void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most k segments of U loads are still in flight (0 <= k < kRingInflight)
+template <int U>
+DEV void ring_wait_segs(int k) {
+  static_assert(kRingInflight <= 11, "one case per segment count");
+  switch (k) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<U * 1>(); break;
+    case 2: vm_wait<U * 2>(); break;
+    case 3: vm_wait<U * 3>(); break;
+    case 4: vm_wait<U * 4>(); break;
+    case 5: vm_wait<U * 5>(); break;
+    case 6: vm_wait<U * 6>(); break;
+    case 7: vm_wait<U * 7>(); break;
+    case 8: vm_wait<U * 8>(); break;
+    case 9: vm_wait<U * 9>(); break;
+    default: vm_wait<U * 10>(); break;
+  }
+}
+
+typedef __attribute__((address_space(1))) const void g_cvoid;
+typedef __attribute__((address_space(3))) void l_void;
+// LDS word access for the loader wavefronts.  The compiler cannot tell the
+// ring's LDS-DMA destinations from other LDS words, so before any LDS access
+// it can see it waits for every LDS-DMA load in flight (vmcnt(0)), which would
+// leave one segment in flight.  These two are invisible to that analysis;
+// each waits for its own LDS operation inside the asm block.
+DEV u32 lds_addr(const void* p) { return (u32)(uintptr_t)(const __attribute__((address_space(3))) char*)p; }
+DEV int lds_rd(const int* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);
+}
+DEV void lds_wr(int* p, int v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// segment `seg` of the tile at w (U KB at byte offset seg * U KB) into one slot
+template <int U>
+DEV void ring_issue(const uint16_t* w, int seg, char* slot, int lane) {
+  const char* src = (const char*)w + (size_t)seg * (U * 1024) + lane * 16;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    __builtin_amdgcn_global_load_lds((g_cvoid*)(src + u * 1024), (l_void*)(slot + u * 1024), 16, 0, AUX_NT);
+}
+
+DEV int ring_nr(const Task& t, const OpDesc& op) { return op.kind == OP_GATEUP ? 2 * t.a2 : t.a2; }
+
+// Spin budget check of the ring's LDS waits (they end by construction; the
+// budget only turns a protocol bug into a reported error instead of a hang).
+DEV bool ring_spin_over(Ctx& c, u64 t0, int it) {
+  if ((it & 63) != 63) return false;
+  if (lds_rd(c.flags)) return true;
+  if (wall_clock64() - t0 > c.a->budget) {
+    if ((threadIdx.x & 63) == 0) report_timeout(*c.a, c.id, -1, 0, 0);
+    lds_wr(c.flags, 1);
+    return true;
+  }
+  return false;
+}
+
+// Loader j (wavefront 4 + j): issues this tile's remaining segments q = j
+// mod 4, publishes each one as it lands, then runs ahead into the next tile when
+// it is a ring tile too.  Returns once every segment of this tile that it
+// loads has landed.
+template <int U>
+DEV void ring_loader(Ctx& c, const OpDesc& op, int q0, int nseg, int j) {
+  int* F = c.flags;
+  const int lane = threadIdx.x & 63;
+  char* ring = c.lds + kRingBase;
+  int qi = lds_rd(F + kFrQi + j), qp = lds_rd(F + kFrQp + j);
+  const uint16_t* W = op.w + (size_t)(u32)c.t.a3;
+  // the next task of this worker, when it is a ring tile (persistent mode)
+  const uint16_t* W2 = nullptr;
+  int nseg2 = 0;
+  if (c.next >= 0) {
+    const Task t2 = c.a->tasks[c.next];
+    const OpDesc& o2 = c.a->ops[t2.op];
+    if (o2.pad & 4) {
+      W2 = o2.w + (size_t)(u32)t2.a3;
+      nseg2 = ring_nr(t2, o2) * ((o2.K * 2) / (U * 1024));
+    }
+  }
+  auto publish = [&]() {  // the oldest segment of this loader in flight has landed
+    // the vmcnt wait orders the slot's LDS-DMA writes before the flag store
+    ring_wait_segs<U>((qi - qp) / kRingLoaders - 1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    lds_wr(F + kFrFill + qp % kRingSlots, qp);
+    qp += kRingLoaders;
+  };
+  auto slot_free = [&](int q) { return lds_rd(F + kFrSlot + q % kRingSlots) == q; };
+  const int qend = q0 + nseg;
+  const u64 t0 = wall_clock64();
+  int it = 0;
+  while (qi < qend) {
+    if ((qi - qp) / kRingLoaders == kRingInflight) {
+      publish();
+    } else if (slot_free(qi)) {
+      ring_issue<U>(W, qi - q0, ring + (qi % kRingSlots) * 4096, lane);
+      qi += kRingLoaders;
+    } else if (qi > qp) {
+      publish();
+    } else {
+      __builtin_amdgcn_s_sleep(1);
+      if (ring_spin_over(c, t0, ++it)) break;
+    }
+  }
+  if (W2 && !lds_rd(F)) {
+    if (j == 0) {
+      lds_wr(F + kFrAhead, c.next);
+      lds_wr(F + kFrAheadQ0, qend);
+    }
+    // publish this tile's segments as they land and keep issuing the next
+    // tile's until the consumers are done with this one; then return with up
+    // to kRingInflight loads in flight (the next task publishes them)
+    for (int it2 = 0;;) {
+      if (qp >= qend && lds_rd(F + kFrDone) == kRingCons) break;
+      if (qi < qend + nseg2 && (qi - qp) / kRingLoaders < kRingInflight && slot_free(qi)) {
+        ring_issue<U>(W2, qi - qend, ring + (qi % kRingSlots) * 4096, lane);
+        qi += kRingLoaders;
+      } else if (qp < qend) {
+        publish();
+      } else {
+        __builtin_amdgcn_s_sleep(1);
+        if (ring_spin_over(c, t0, ++it2)) break;
+      }
+    }
+  } else {
+    while (qp < qi) publish();
+  }
+  lds_wr(F + kFrQi + j, qi);
+  lds_wr(F + kFrQp + j, qp);
+}
+
+// Consumer wavefronts 0..3: segments s = wave, wave + 4, ... of this tile.
+template <int U>
+DEV void ring_consume(Ctx& c, const OpDesc& op, int q0, int nseg, int spr, const float* xs, float* part, int wave,
+                      int lane) {
+  int* F = c.flags;
+  char* ring = c.lds + kRingBase;
+  const bool early = (op.pad & 2) != 0;
+  const u64 t0 = wall_clock64();
+  int it = 0;
+  for (int s = wave; s < nseg; s += kRingCons) {
+    const int q = q0 + s, slot = q % kRingSlots;
+    while (__hip_atomic_load(F + kFrFill + slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != q) {
+      __builtin_amdgcn_s_sleep(1);
+      if (ring_spin_over(c, t0, ++it)) return;
+    }
+    const int col0 = (s % spr) * (U * 512);
+    const char* sp = ring + slot * 4096 + lane * 16;
+    const float* xp = xs + col0 + lane * 8;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4 w = *(const u32x4*)(sp + u * 1024);
+      const f32x4 x0 = *(const f32x4*)(xp + u * 512);
+      const f32x4 x1 = *(const f32x4*)(xp + u * 512 + 4);
+      acc = fmaf(bf_lo(w.x), x0.x, acc);
+      acc = fmaf(bf_hi(w.x), x0.y, acc);
+      acc = fmaf(bf_lo(w.y), x0.z, acc);
+      acc = fmaf(bf_hi(w.y), x0.w, acc);
+      acc = fmaf(bf_lo(w.z), x1.x, acc);
+      acc = fmaf(bf_hi(w.z), x1.y, acc);
+      acc = fmaf(bf_lo(w.w), x1.z, acc);
+      acc = fmaf(bf_hi(w.w), x1.w, acc);
+    }
+    const float v = wave_sum(acc);  // every lane's slot reads are complete here
+    if (lane == 0) {
+      part[s] = v;
+      __hip_atomic_store(F + kFrSlot + slot, q + kRingSlots, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    // early trigger once about kEarlySegments segments per wavefront remain
+    if (early && wave == 0 && s + kRingCons * kEarlySegments >= nseg && lane == 0) trigger_event(c);
+  }
+}
+
+// Input staging by the consumer wavefronts: xs[k] = in[k] * g[k]; returns this
+// thread's sum of in[k]^2.
+DEV float ring_stage(Ctx& c, const OpDesc& op, int tid, float* xs) {
+  const StepArgs& a = *c.a;
+  const int K = op.K;
+  constexpr int CH = kRingStageCH, T = kRingThreads;
+  float ss = 0.f;
+  // buffer loads: one resource and one register offset for all words (words
+  // past K read as zero and are not used)
+  const __amdgpu_buffer_rsrc_t rin = rsrc_u(op.in, (u32)K * 8u);
+  const __amdgpu_buffer_rsrc_t rg =
+      rsrc_u(op.g, op.norm_in ? (u32)K * 4u : 0u);
+  for (int base = 0; base < K; base += CH * T) {  // base: the same in every lane (scalar offsets)
+    const int k0 = base + tid;
+    u64 w[CH];
+    float gv[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rin, (u32)tid * 8u, (base + i * T) * 8, 0);
+      w[i] = ((u64)v.y << 32) | v.x;
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      gv[i] = op.norm_in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (u32)tid * 4u, (base + i * T) * 4, 0))
+                         : 1.0f;
+    refresh_batch<CH>(w, op.in, k0, T, K, a);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int k = k0 + i * T;
+      if (k < K) {
+        const float v = __uint_as_float((u32)w[i]);
+        xs[k] = v * gv[i];
+        ss += v * v;
+      }
+    }
+  }
+  return ss;
+}
+
+DEV const float* ring_rows(const Ctx& c) { return (const float*)(c.lds + kRingRows); }
+
+template <int U>
+DEV void gemv_ring(Ctx& c, const OpDesc& op) {
+  const StepArgs& a = *c.a;
+  int* F = c.flags;
+  const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
+  const int nr = c.t.a2, NR = ring_nr(c.t, op);
+  const int spr = (op.K * 2) / (U * 1024), nseg = NR * spr;
+  float* xs = (float*)(c.lds + kRingXs);
+  float* part = (float*)(c.lds + kRingPart);
+  float* red = (float*)(F + 8);      // per consumer wavefront: sum of squares
+  float* rnp = red + NWAVE;          // the norm scale (where lm_candidates reads it for NB = 1)
+  // ring state: continue a run-ahead into this tile, or start an empty ring
+  int q0 = 0;
+  const bool ahead = lds_rd(F + kFrAhead) == c.id;  // (loaders may have LDS-DMA loads in flight)
+  if (ahead) q0 = lds_rd(F + kFrAheadQ0);
+  __syncthreads();  // every wavefront has read the state above
+  if (!ahead) {
+    if (tid < kRingLoaders) {
+      F[kFrQi + tid] = tid;
+      F[kFrQp + tid] = tid;
+    }
+    if (tid < kRingSlots) {
+      F[kFrSlot + tid] = tid;
+      F[kFrFill + tid] = -1;
+    }
+  }
+  if (tid == 0) {
+    F[kFrAhead] = -1;
+    F[kFrGo] = 0;
+    F[kFrStaged] = 0;
+    F[kFrDone] = 0;
+  }
+  __syncthreads();
+  u64 res0 = 0;
+  if (wave >= kRingCons) {
+    ring_loader<U>(c, op, q0, nseg, wave - kRingCons);
+  } else {
+    // dependency: wavefront 0 polls, the other consumers wait for its flag
+    if (wave == 0) {
+      poll_dep(c);
+      if (lane == 0) __hip_atomic_store(F + kFrGo, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      const u64 t0 = wall_clock64();
+      int it = 0;
+      while (!__hip_atomic_load(F + kFrGo, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++it & 1023) == 0 && wall_clock64() - t0 > (u64)2 * a.budget) break;  // wavefront 0 has its own watchdog
+      }
+    }
+    const float ss = wave_sum(ring_stage(c, op, tid, xs));
+    res0 = gemv_residual_prefetch(c, op, 1);
+    if (lane == 0) {
+      red[wave] = ss;
+      __hip_atomic_fetch_add(F + kFrStaged, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    {
+      const u64 t0 = wall_clock64();
+      int it = 0;
+      while (__hip_atomic_load(F + kFrStaged, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kRingCons) {
+        __builtin_amdgcn_s_sleep(1);
+        if (ring_spin_over(c, t0, ++it)) break;
+      }
+    }
+    if (tid == 0) {
+      float s = 0.f;
+      for (int w = 0; w < kRingCons; ++w) s += red[w];
+      *rnp = op.norm_in ? rsqrtf(s / (float)op.K + a_eps(c)) : 1.0f;
+    }
+    ring_consume<U>(c, op, q0, nseg, spr, xs, part, wave, lane);
+    // the consumers' own barrier: the loaders keep streaming meanwhile
+    if (lane == 0) __hip_atomic_fetch_add(F + kFrDone, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    {
+      const u64 t0 = wall_clock64();
+      int it = 0;
+      while (__hip_atomic_load(F + kFrDone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kRingCons) {
+        __builtin_amdgcn_s_sleep(1);
+        if (ring_spin_over(c, t0, ++it)) break;
+      }
+    }
+  }
+  // epilogue (consumer threads only: the loader wavefronts may still have
+  // run-ahead loads in flight and issue no other memory operations); the
+  // task's closing barrier in finish() joins the loaders
+  if (tid < kRingThreads) {
+    const float rn = *rnp;
+    float* rows = (float*)(c.lds + kRingRows);
+    const int r0 = c.t.a1;
+    for (int j = tid; j < nr; j += kRingThreads) {
+      float sv = 0.f;
+      for (int i = 0; i < spr; ++i) sv += part[j * spr + i];
+      const float v = sv * rn;
+      const int row = r0 + j;
+      switch (op.kind) {
+        case OP_QKV:
+          st_t(op.out + row, v, a.tag);
+          break;
+        case OP_OPROJ:
+        case OP_DOWN: {
+          const u64* rp = op.res + row;
+          const float rv = j == tid ? fix_t(res0, rp, a) : ld_t(rp, a);
+          st_t(op.out + row, rv + v, a.tag);
+          break;
+        }
+        case OP_GATEUP: {
+          float su = 0.f;
+          for (int i = 0; i < spr; ++i) su += part[(nr + j) * spr + i];
+          st_t(op.out + row, silu(v) * (su * rn), a.tag);
+          break;
+        }
+        case OP_LMHEAD:
+          a.logits[row] = v;
+          rows[j] = sv;
+          break;
+        default:
+          break;
+      }
+    }
+  }
+}
+
+DEV void gemv_ring_any(Ctx& c, const OpDesc& op) {
+  const int u = c.a->geom->ring_u;
+  if (u == 4) gemv_ring<4>(c, op);
+  else if (u == 2) gemv_ring<2>(c, op);
+  else gemv_ring<1>(c, op);
+}
+
 // ---------------------------------------------------------------- GEMV (MFMA, batch 5..16)
 // A skinny GEMM on the matrix cores: D[16 rows][16 sequences] += W[16][32] x
 // X[32][16] per v_mfma_f32_16x16x32_bf16, sequences past the batch padded
@@ -935,7 +1351,7 @@ DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
   const int NJp = (NJ + DEPTH - 1) / DEPTH * DEPTH;
   const uint16_t* Wt = op.w + (size_t)(u32)t.a3;
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, (int)((u32)NR * (u32)K * 2u), 0x00020000);
+      rsrc_u(Wt, (u32)NR * (u32)K * 2u);
 
   // fill cursor: chunk fc, item slot fit (its group fg and part fqp), step fj
   int fc = 0, fit = 0, fj = 0;
@@ -1255,9 +1671,9 @@ DEV void attn_chunk(Ctx& c, const OpDesc& op) {
     return ((u32)((pgl[(t >> sh) - lp0] * Hkv + gi) << sh) + (u32)(t & pmask)) * (u32)D;
   };
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? Kc : Kc + (size_t)t0 * D), 0, (int)span, 0x00020000);
+      rsrc_u(paged ? Kc : Kc + (size_t)t0 * D, (u32)span);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? Vc : Vc + (size_t)t0 * D), 0, (int)span, 0x00020000);
+      rsrc_u(paged ? Vc : Vc + (size_t)t0 * D, (u32)span);
   const int krow = wave * KR + lane / KL, kc = lane % KL;  // key row within a pass, 16-byte column
   const int vrow = wave * VR + lane / VL, vc = lane % VL;  // value row within a pass, 4-byte column
   auto koff = [&](int p) -> u32 {
@@ -1671,8 +2087,7 @@ DEV void moe_gu_items(Ctx& c, const OpDesc& op, const float* xs, const int* s_ac
   const int U = Ie / 16;
   constexpr int NL = 4 * NCH, DEPTH = MoeRing<NL>::DEPTH;
   // weights of every expert: [E][2*Ie][H]; unit u of e starts at row e*2*Ie + 32u
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)op.w, (short)0, (int)((u32)G.E * 2u * (u32)Ie * (u32)H * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = rsrc_u(op.w, (u32)G.E * 2u * (u32)Ie * (u32)H * 2u);
   auto rowbase = [&](int it) -> int {  // this wavefront's first row of item it (-1 past the share)
     if (it >= i1) return -1;
     const int e = s_act[it / U];
@@ -1798,8 +2213,7 @@ DEV void body_moe_down(Ctx& c, const OpDesc& op) {
   const int i0 = (int)((long)s * total / ns), i1 = (int)((long)(s + 1) * total / ns);
   if (i1 <= i0) return;
   const int nchunk = (Ie / 8 + 63) / 64;  // Ie = 768: 2
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)op.w, (short)0, (int)((u32)G.E * (u32)H * (u32)Ie * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = rsrc_u(op.w, (u32)G.E * (u32)H * (u32)Ie * 2u);
   constexpr int DEPTH = 8;
   const int NL = 8 * nchunk;  // loads per item per lane: 8 rows x nchunk chunks (a multiple of DEPTH)
   auto rowbase = [&](int it) -> int {  // this wavefront's first row of item it (-1 past the share)

@@ -953,6 +953,38 @@ uint32_t graph_magic(const Graph& g) {
   return h | 1u;
 }
 
+// With opts.lds_ring, batch-1 VALU GEMV tiles whose rows are whole kilobytes
+// and whose input, segments and rows fit the LDS ring's areas are fed through
+// the LDS weight ring (loader wavefronts stream the weights, see device.h).  The segment
+// size, in KB, is the largest of 4, 2, 1 dividing every such op's row bytes
+// (one size per graph, so that segments of consecutive tiles can share the
+// loader's in-flight accounting).  Returns it, or 0 when no op qualifies.
+static int32_t assign_ring(Graph& g) {
+  if (g.B != 1 || g.gemv != MK_GEMV_VALU || !g.opts.lds_ring) return 0;
+  std::vector<int32_t> max_rows(g.ops.size(), 0);
+  for (const Task& t : g.tasks) {
+    const OpInst& o = g.ops[(size_t)t.op];
+    if (o.kind == OP_QKV || o.kind == OP_OPROJ || o.kind == OP_GATEUP || o.kind == OP_DOWN || o.kind == OP_LMHEAD)
+      max_rows[(size_t)t.op] = std::max(max_rows[(size_t)t.op], o.kind == OP_GATEUP ? 2 * t.a2 : t.a2);
+  }
+  int32_t u = 4;
+  std::vector<size_t> cand;
+  for (size_t i = 0; i < g.ops.size(); ++i) {
+    const OpInst& o = g.ops[i];
+    if (max_rows[i] == 0 || o.K % 512 != 0 || o.K > kRingMaxK || max_rows[i] > kRingMaxRows) continue;
+    while ((o.K * 2) % (u * 1024) != 0) u /= 2;
+    cand.push_back(i);
+  }
+  // segments per tile must fit the partials area (dropping an op keeps u valid)
+  bool any = false;
+  for (size_t i : cand) {
+    if ((int64_t)max_rows[i] * (g.ops[i].K * 2 / (u * 1024)) > kRingMaxSegs) continue;
+    g.ops[i].ring = true;
+    any = true;
+  }
+  return any ? u : 0;
+}
+
 Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, const mk_build_opts& o, int32_t workers,
                        bool fuse, std::string* err) {
   auto bad = [&](const char* m) -> Graph* {
@@ -979,8 +1011,9 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   if (batch <= 0 || batch > 16) return bad("batch must be in 1..16");
   if (cap <= 0 || cap > (1 << 20)) return bad("max_ctx out of range");
   if (workers <= 0 || workers > 4096) return bad("worker count out of range");
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 3; ++i)
     if (o.reserved[i]) return bad("reserved options must be zero");
+  if (o.lds_ring < 0 || o.lds_ring > 1) return bad("lds_ring must be 0 or 1");
   if (o.prefetch_loads < 0 || o.prefetch_loads > 64) return bad("prefetch_loads must be in 0..64");
   if (o.trace < 0 || o.trace > 2) return bad("trace must be 0, 1 or 2");
   if (o.no_watchdog && s.n_experts > 0) return bad("no_watchdog: routed-expert graphs need the dispatch wavefront");
@@ -1040,6 +1073,7 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   }
   layout(*g);
   Geom& ge = g->geom;
+  ge.ring_u = assign_ring(*g);
   ge.B = batch;
   ge.H = s.hidden;
   ge.Hq = s.n_q_heads;

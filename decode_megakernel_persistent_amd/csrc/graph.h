@@ -25,6 +25,7 @@ struct OpInst {
   int64_t w_off = -1;                 // arena byte offset of the weight block
   int64_t g_off = -1, g2_off = -1;    // arena byte offsets of fp32 gains
   int32_t in_buf = -1, res_buf = -1, out_buf = -1, aux_buf = -1, aux2_buf = -1;
+  bool ring = false;                  // batch-1 GEMV tiles fed through the LDS weight ring
 };
 
 // Activation buffer in scratch (tagged 64-bit words), or a virtual buffer

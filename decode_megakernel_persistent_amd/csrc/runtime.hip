@@ -39,7 +39,7 @@ namespace mk {
 
 // ---------------------------------------------------------------- kernels
 template <int NB, bool MULTI>
-DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int* flags, const int* pos) {
+DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int* flags, const int* pos, int next) {
   Ctx c;
   c.a = &a;
   c.t = a.tasks[id];
@@ -49,6 +49,7 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
   c.lds = lds;
   c.flags = flags;
   c.pos = pos;
+  c.next = next;
   if (threadIdx.x == 0) {
     flags[5] = 0;  // not triggered yet (read after the body's barriers)
     if (a.trace_on == 2) flags[kFlagEntryClock] = (int)(u32)wall_clock64();
@@ -62,7 +63,10 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
     case OP_LMHEAD:
     case OP_ROUTER:
       if constexpr (NB == kMfmaVariant) gemv_mfma(c, op);
-      else gemv_valu_any<NB>(c, op);
+      else if constexpr (NB == kRingVariant) {
+        if (op.pad & 4) gemv_ring_any(c, op);
+        else gemv_valu_any<1>(c, op);
+      } else gemv_valu_any<NB>(c, op);
       break;
     case OP_ATTN:
       body_attn(c, op);
@@ -98,7 +102,14 @@ DEV void run_task(const StepArgs& a, int id, int agent, bool lpt, char* lds, int
   if constexpr (MULTI) {
     if (op.kind == OP_LMHEAD && a.cand) {
       if constexpr (NB == kMfmaVariant) lm_candidates(c, mfma_rows(c), c.t.a2, mfma_scales(c), a.geom->B);
-      else lm_candidates(c, valu_rows(c), c.t.a2, valu_scales(c, NB), NB);
+      else if constexpr (NB == kRingVariant) {
+        if (op.pad & 4) {
+          __syncthreads();  // the ring epilogue's row sums, written by other threads
+          lm_candidates(c, ring_rows(c), c.t.a2, valu_scales(c, 1), 1);
+        } else {
+          lm_candidates(c, valu_rows(c), c.t.a2, valu_scales(c, 1), 1);
+        }
+      } else lm_candidates(c, valu_rows(c), c.t.a2, valu_scales(c, NB), NB);
     }
   }
   finish(c);
@@ -119,6 +130,7 @@ DEV bool entry_ok(const StepArgs& a, int* flags, int* pos) {
     // a failed step leaves the error word set until mk_check clears it
     if (__hip_atomic_load(a.status + ST_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ok = 0;
     flags[0] = ok ? 0 : 1;
+    flags[kFrAhead] = -1;  // no LDS-ring run-ahead pending
   }
   __syncthreads();
   return flags[0] == 0;
@@ -132,10 +144,16 @@ DEV bool entry_ok(const StepArgs& a, int* flags, int* pos) {
 // token feedback.  Separate instantiations keep the outer step loop and the
 // candidate code out of the one-step kernel, where they measurably slowed the
 // bodies (register and instruction-cache pressure, ~1.3% of a step).
+// (the attribute takes a literal constant, so the unit macro picks the cap)
+#if defined(MK_UNIT_NB) && (MK_UNIT_NB == 1 || MK_UNIT_NB == 17)
+#define MK_WORKER_VGPRS kWorkerVgprsB1
+#else
+#define MK_WORKER_VGPRS kWorkerVgprs
+#endif
 template <int NB, bool MULTI>
-__global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerVgprs))) mk_worker(StepArgs a) {
+__global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(MK_WORKER_VGPRS))) mk_worker(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int flags[64];
+  __shared__ int flags[kFlagWords];
   __shared__ int pos[16];
   // arrival and completion count one per step, so that the dispatch
   // wavefront's targets (workers x persistent steps so far) hold for any mix
@@ -145,12 +163,13 @@ __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerV
   if (entry_ok(a, flags, pos)) {
     const int w = blockIdx.x;
     if constexpr (!MULTI) {
-      for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
+      const int kend = a.wl_off[w + 1];
+      for (int k = a.wl_off[w]; k < kend; ++k) {
         if (threadIdx.x == 0)
           __hip_atomic_store(a.progress + w, (u32)a.wl_ids[k] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        run_task<NB, false>(a, a.wl_ids[k], w, false, lds, flags, pos);
+        run_task<NB, false>(a, a.wl_ids[k], w, false, lds, flags, pos, k + 1 < kend ? a.wl_ids[k + 1] : -1);
         __syncthreads();
-        if (flags[0]) break;
+        if (lds_rd(flags)) break;  // (not ordered behind the LDS-ring loader's loads in flight)
       }
     } else {
       // Multi-step decode: the same task list once per step, with the step's
@@ -164,12 +183,13 @@ __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerV
           if ((int)threadIdx.x < a.geom->B) pos[threadIdx.x] = a.positions[threadIdx.x] + s;
           __syncthreads();
         }
-        for (int k = a.wl_off[w]; k < a.wl_off[w + 1]; ++k) {
+        const int kend = a.wl_off[w + 1];
+        for (int k = a.wl_off[w]; k < kend; ++k) {
           if (threadIdx.x == 0)
             __hip_atomic_store(a.progress + w, (u32)a.wl_ids[k] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          run_task<NB, true>(a, a.wl_ids[k], w, false, lds, flags, pos);
+          run_task<NB, true>(a, a.wl_ids[k], w, false, lds, flags, pos, k + 1 < kend ? a.wl_ids[k + 1] : -1);
           __syncthreads();
-          if (flags[0]) break;
+          if (lds_rd(flags)) break;
         }
         if (flags[0]) break;
         if (s + 1 < n) {
@@ -188,6 +208,7 @@ __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerV
         c.lds = lds;
         c.flags = flags;
         c.pos = pos;
+        c.next = -1;
         int* tk = (int*)lds;
         lm_argmax(c, a.epoch + 1u, a.tag, 0, a.geom->B, tk);
         if ((int)threadIdx.x < a.geom->B && !flags[0])
@@ -204,9 +225,9 @@ __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(kWorkerV
 template <int NB>
 __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int flags[64];
+  __shared__ int flags[kFlagWords];
   __shared__ int pos[16];
-  if (entry_ok(a, flags, pos)) run_task<NB, false>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags, pos);
+  if (entry_ok(a, flags, pos)) run_task<NB, false>(a, a.lpt_first + (int)blockIdx.x, -1, true, lds, flags, pos, -1);
 }
 
 #if defined(MK_UNIT_ALL) || (defined(MK_UNIT_NB) && MK_UNIT_NB == 1)
@@ -215,7 +236,11 @@ __global__ void __launch_bounds__(NT, 1) mk_lpt(StepArgs a) {
 // has finished the step, raising the abort flag if that takes longer than the
 // watchdog budget.  Bounded to 64 VGPRs (8 waves per SIMD): two worker
 // wavefronts of up to 224 registers and this one must share a SIMD's 512.
-__global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) {
+// Graphs without dispatcher tasks (dense models) launch mk_dispatch_dense,
+// the same wavefront without the routing code, bounded to 32 VGPRs, which
+// leaves two worker wavefronts 240 registers each.
+template <bool ROUTED>
+DEV void dispatch_body(StepArgs& a) {
   const int W = a.n_workers;
   // launch-per-task steps advance the epoch but not the workers' arrival and
   // completion counts, so the targets count persistent steps only
@@ -243,7 +268,7 @@ __global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) {
     __builtin_amdgcn_s_sleep(16);
   }
   // the dispatcher's own tasks (routing of routed-expert layers), in id order
-  {
+  if constexpr (ROUTED) {
     __shared__ int flags[64];
     if (threadIdx.x < 64) flags[threadIdx.x] = 0;
     __syncthreads();
@@ -266,6 +291,7 @@ __global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) {
         c.lds = nullptr;
         c.flags = flags;
         c.pos = nullptr;
+        c.next = -1;
         if (threadIdx.x == 0) {
           flags[5] = 0;
           if (a.trace_on == 2) flags[kFlagEntryClock] = (int)(u32)wall_clock64();
@@ -277,9 +303,9 @@ __global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) {
         __syncthreads();
       }
     }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(a.progress + W, 0xFFFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.progress + W, 0xFFFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   t0 = wall_clock64();
   for (;;) {
     u32 done = __hip_atomic_load(a.status + ST_DONE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -292,8 +318,11 @@ __global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) {
     __builtin_amdgcn_s_sleep(127);
   }
 }
+__global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a) { dispatch_body<true>(a); }
+__global__ void __launch_bounds__(64, 16) mk_dispatch_dense(StepArgs a) { dispatch_body<false>(a); }
 #else
 __global__ void __launch_bounds__(64, 8) mk_dispatch(StepArgs a);
+__global__ void __launch_bounds__(64, 16) mk_dispatch_dense(StepArgs a);
 #endif
 
 #if defined(MK_UNIT_NB)
@@ -309,16 +338,19 @@ extern template __global__ void mk_worker<2, false>(StepArgs);
 extern template __global__ void mk_worker<3, false>(StepArgs);
 extern template __global__ void mk_worker<4, false>(StepArgs);
 extern template __global__ void mk_worker<kMfmaVariant, false>(StepArgs);
+extern template __global__ void mk_worker<kRingVariant, false>(StepArgs);
 extern template __global__ void mk_worker<1, true>(StepArgs);
 extern template __global__ void mk_worker<2, true>(StepArgs);
 extern template __global__ void mk_worker<3, true>(StepArgs);
 extern template __global__ void mk_worker<4, true>(StepArgs);
 extern template __global__ void mk_worker<kMfmaVariant, true>(StepArgs);
+extern template __global__ void mk_worker<kRingVariant, true>(StepArgs);
 extern template __global__ void mk_lpt<1>(StepArgs);
 extern template __global__ void mk_lpt<2>(StepArgs);
 extern template __global__ void mk_lpt<3>(StepArgs);
 extern template __global__ void mk_lpt<4>(StepArgs);
 extern template __global__ void mk_lpt<kMfmaVariant>(StepArgs);
+extern template __global__ void mk_lpt<kRingVariant>(StepArgs);
 #endif
 
 }  // namespace mk
@@ -327,8 +359,10 @@ extern template __global__ void mk_lpt<kMfmaVariant>(StepArgs);
 #if defined(MK_UNIT_ALL) || defined(MK_UNIT_HOST)
 namespace mk {
 // Kernel variants: 1..4 = VALU GEMV for that batch, kMfmaVariant = MFMA GEMV
-// (any batch up to 16).  Separate instantiations keep each one's register
-// allocation to the GEMV it actually runs.
+// (any batch up to 16), kRingVariant = batch 1 with the LDS weight ring.
+// Separate instantiations keep each one's register allocation to the GEMV it
+// actually runs (compiling the ring into the batch-1 worker cost ~3% of its
+// step even with the ring unused).
 typedef void (*kernel_fn)(StepArgs);
 static const void* worker_fn(int v, bool multi) {
   if (multi) {
@@ -337,6 +371,7 @@ static const void* worker_fn(int v, bool multi) {
       case 2: return (const void*)mk_worker<2, true>;
       case 3: return (const void*)mk_worker<3, true>;
       case 4: return (const void*)mk_worker<4, true>;
+      case kRingVariant: return (const void*)mk_worker<kRingVariant, true>;
       default: return (const void*)mk_worker<kMfmaVariant, true>;
     }
   }
@@ -345,6 +380,7 @@ static const void* worker_fn(int v, bool multi) {
     case 2: return (const void*)mk_worker<2, false>;
     case 3: return (const void*)mk_worker<3, false>;
     case 4: return (const void*)mk_worker<4, false>;
+    case kRingVariant: return (const void*)mk_worker<kRingVariant, false>;
     default: return (const void*)mk_worker<kMfmaVariant, false>;
   }
 }
@@ -354,10 +390,13 @@ static const void* lpt_fn(int v) {
     case 2: return (const void*)mk_lpt<2>;
     case 3: return (const void*)mk_lpt<3>;
     case 4: return (const void*)mk_lpt<4>;
+    case kRingVariant: return (const void*)mk_lpt<kRingVariant>;
     default: return (const void*)mk_lpt<kMfmaVariant>;
   }
 }
-static int kernel_variant(const Graph& G) { return G.gemv == MK_GEMV_MFMA ? kMfmaVariant : G.B; }
+static int kernel_variant(const Graph& G) {
+  return G.gemv == MK_GEMV_MFMA ? kMfmaVariant : G.geom.ring_u > 0 ? kRingVariant : G.B;
+}
 
 }  // namespace mk
 
@@ -606,7 +645,8 @@ mk_status launch_step(mk_graph* g, StepArgs& a, bool multi, hipStream_t stream) 
     }
     if (watch) {
       HIPCHK(hipStreamWaitEvent(side, (hipEvent_t)g->ev_a, 0));
-      hipLaunchKernelGGL(mk_dispatch, dim3(1), dim3(64), 0, side, a);
+      if (G.wl_off[G.W + 1] > G.wl_off[G.W]) hipLaunchKernelGGL(mk_dispatch, dim3(1), dim3(64), 0, side, a);
+      else hipLaunchKernelGGL(mk_dispatch_dense, dim3(1), dim3(64), 0, side, a);
       HIPCHK(hipGetLastError());
       HIPCHK(hipEventRecord((hipEvent_t)g->ev_b, side));
       HIPCHK(hipStreamWaitEvent(stream, (hipEvent_t)g->ev_b, 0));
@@ -838,7 +878,8 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
     d.norm_in = o.norm_in;
     d.ntasks = o.ntasks;
     d.pre = G.opts.prefetch_loads > 0 ? G.opts.prefetch_loads : default_prefetch_loads(o.kind);
-    d.pad = (ctrl_wave_kinds(o.kind) ? 1 : 0) | (early_trigger_kinds(o.kind) && !G.opts.late_trigger ? 2 : 0);
+    d.pad = (ctrl_wave_kinds(o.kind) ? 1 : 0) | (early_trigger_kinds(o.kind) && !G.opts.late_trigger ? 2 : 0) |
+            (o.ring ? 4 : 0);
     d.w = o.w_off >= 0 ? (const uint16_t*)(arena + o.w_off) : nullptr;
     d.g = o.g_off >= 0 ? (const float*)(arena + o.g_off) : nullptr;
     d.g2 = o.g2_off >= 0 ? (const float*)(arena + o.g2_off) : nullptr;
@@ -879,7 +920,7 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   HIPCHK(hipDeviceGetAttribute(&wcr, hipDeviceAttributeWallClockRate, dev));
   const int64_t us = G.opts.spin_timeout_us > 0 ? G.opts.spin_timeout_us : 2000000;
   g->budget_ticks = (uint64_t)us * (uint64_t)(wcr > 0 ? wcr : 100000) / 1000ull;
-  for (int v : {1, 2, 3, 4, (int)kMfmaVariant}) {
+  for (int v : {1, 2, 3, 4, (int)kMfmaVariant, (int)kRingVariant}) {
     (void)hipFuncSetAttribute(worker_fn(v, false), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     (void)hipFuncSetAttribute(worker_fn(v, true), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     (void)hipFuncSetAttribute(lpt_fn(v), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
@@ -890,11 +931,13 @@ mk_status mk_load_weights(mk_graph* g, const mk_tensor* tensors, int32_t n, void
   for (bool multi : {false, true}) {
     hipFuncAttributes fw, fd;
     HIPCHK(hipFuncGetAttributes(&fw, worker_fn(kernel_variant(G), multi)));
-    HIPCHK(hipFuncGetAttributes(&fd, (const void*)mk_dispatch));
+    const bool routed = G.wl_off[G.W + 1] > G.wl_off[G.W];
+    HIPCHK(hipFuncGetAttributes(&fd, routed ? (const void*)mk_dispatch : (const void*)mk_dispatch_dense));
     auto gran = [](int v) { return (v + 7) / 8 * 8; };
     if (2 * gran(fw.numRegs) + gran(fd.numRegs) > 512 || fw.localSizeBytes > 0) {
       set_error("mk_load_weights: worker kernel uses " + std::to_string(fw.numRegs) + " VGPRs and " +
-                std::to_string(fw.localSizeBytes) + " B scratch; the dispatch wavefront would not fit beside it");
+                std::to_string(fw.localSizeBytes) + " B scratch; the dispatch wavefront would not fit beside it" +
+                (routed ? " (routed experts at batch 1 need gemv = MK_GEMV_MFMA)" : ""));
       return MK_ERR_NOT_RESIDENT;
     }
   }
@@ -1320,6 +1363,9 @@ mk_status mk_graph_stats(const mk_graph* g, mk_stats* out) {
   out->max_ctx = G.cap;
   out->attn_chunks = G.C;
   out->gemv = G.gemv;
+  out->ring_kb = G.geom.ring_u;
+  out->ring_ops = 0;
+  for (const OpInst& o : G.ops) out->ring_ops += o.ring ? 1 : 0;
   return MK_OK;
 }
 

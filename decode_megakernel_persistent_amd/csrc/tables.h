@@ -61,7 +61,8 @@ struct OpDesc {
   int32_t norm_in;   // 1: input is rmsnorm(in) * g
   int32_t ntasks;
   int32_t pre;       // GEMV: weight loads per lane issued before the dependency wait
-  int32_t pad;
+  int32_t pad;       // bit 0: control wavefront issues no pre-wait loads; bit 1: early trigger;
+                     // bit 2: batch-1 tile fed through the LDS weight ring
   const uint16_t* w; // weight block (bf16)
   const float* g;    // input-norm gain [K] (or q-norm gain [D])
   const float* g2;   // k-norm gain [D]
@@ -85,6 +86,7 @@ struct Geom {
   int32_t mfma;         // 1: GEMV tiles use the MFMA path (swizzled weight fragments)
   int32_t lm_event;     // terminal event of the lm_head tiles (-1: none)
   int32_t lm_tiles;     // lm_head tiles (producers of lm_event)
+  int32_t ring_u;       // KB per LDS-ring segment of batch-1 GEMV tiles (4, 2 or 1), 0 = no ring tiles
   const double* inv_freq;  // RoPE inverse frequencies [D/2]
 };
 
@@ -113,10 +115,15 @@ enum StatusWord : int32_t {
 };
 
 // LDS budget of one worker (bytes) and the areas the task bodies use.
-constexpr int kLdsBytes = 140 * 1024;  // dynamic LDS per worker (gfx950: 160 KB per CU)
+constexpr int kLdsBytes = 156 * 1024;  // dynamic LDS per worker (gfx950: 160 KB per CU)
 constexpr int kStageFloats = 24576;      // GEMV input staging (96 KB)
 constexpr int kRowResultFloats = 8192;   // GEMV per-row results (32 KB)
 constexpr int kScoreFloats = 8192;       // attention scores of one chunk (32 KB)
+// Batch-1 GEMV tiles fed through the LDS weight ring: limits of one tile
+// (input length, segments, rows) that the ring's LDS areas hold.
+constexpr int kRingMaxK = 12288;
+constexpr int kRingMaxSegs = 2048;
+constexpr int kRingMaxRows = 1024;
 
 enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT = 1, ERR_CONFIG = 2, ERR_BAD_TASK = 3, ERR_BAD_INPUT = 4, ERR_NOT_RESIDENT = 5 };
 
@@ -126,6 +133,9 @@ enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT = 1, ERR_CONFIG = 2, ERR_BAD
 // the dispatch wavefront (about 64 registers: it also routes MoE tokens) fit
 // a SIMD's 512, which mk_load_weights checks on the built kernels.
 constexpr int kWorkerVgprs = 248;
+// The batch-1 variant is held to 216 (its SGPR spill lanes come on top; at
+// 232 it would leave the dispatch wavefront less than its 64 registers).
+constexpr int kWorkerVgprsB1 = 216;
 
 // Decode steps one persistent launch may run (mk_decode_steps).
 constexpr int kMaxStepsPerLaunch = 4096;

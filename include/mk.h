@@ -103,7 +103,11 @@ typedef struct {
   int32_t late_trigger;    /* 1 = GEMV tasks trigger their event after storing their outputs;
                               0 = once their last weight loads are issued (consumers re-read
                               words whose step tag is not yet current; default) */
-  int32_t reserved[4];     /* must be zero */
+  int32_t lds_ring;        /* 1 = batch-1 GEMV tiles whose rows are whole KB are fed through an LDS
+                              ring by four loader wavefronts (LDS-DMA loads) that run ahead into the
+                              worker's next tile; 0 = weights stream through registers (default,
+                              faster as measured) */
+  int32_t reserved[3];     /* must be zero */
 } mk_build_opts;
 
 /* One logical tensor handed to mk_load_weights.  Names:
@@ -175,6 +179,8 @@ typedef struct {
   int64_t weight_bytes;      /* weight bytes one step streams (dense) */
   int64_t arena_bytes, scratch_bytes, trace_bytes;
   int32_t batch, max_ctx, attn_chunks, gemv;
+  int32_t ring_kb;           /* KB per LDS-ring segment of batch-1 GEMV tiles, 0 = no ring tiles */
+  int32_t ring_ops;          /* operator instances whose tiles are fed through the LDS ring */
 } mk_stats;
 
 /* Compile the task graph for a model shape, batch and KV capacity (host only;

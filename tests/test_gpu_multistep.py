@@ -110,6 +110,15 @@ def test_8b_multistep_matches_single_steps():
     check_multistep(w, harness.prepare(w), 8)
 
 
+@pytest.mark.parametrize("wname", ["qwen3-0.6b", "qwen3-8b"])
+def test_lds_ring_multistep_matches_single_steps(wname):
+    # the LDS weight ring's loaders run ahead from tile to tile across a whole
+    # multi-step launch: bit-exact against one-step launches, tokens and last
+    # logits against the oracle
+    w = synth.WORKLOADS[wname]
+    check_multistep(w, harness.prepare(w), 8, lds_ring=1)
+
+
 def test_tied_embedding_multistep_crosses_chunk_boundaries():
     # 0.6B (tied lm_head, VALU tiles) for its configured 32 steps in one launch:
     # with 18 chunks over 513..544 positions, rows appended early in the launch

@@ -25,9 +25,10 @@ pytestmark = pytest.mark.gpu
 
 
 def run_steps(w, prep, mode, steps, trace=True, workers=0, gemv=mk.MK_GEMV_AUTO, attn_chunks=0, merge_tasks=0,
-              no_fusion=0, per_task_launch=0, page_size=0):
+              no_fusion=0, per_task_launch=0, page_size=0, lds_ring=0):
     opts = mk.make_opts(mode=mode, trace=int(trace), num_workers=workers, gemv=gemv, attn_chunks=attn_chunks,
-                        merge_tasks=merge_tasks, no_fusion=no_fusion, per_task_launch=per_task_launch)
+                        merge_tasks=merge_tasks, no_fusion=no_fusion, per_task_launch=per_task_launch,
+                        lds_ring=lds_ring)
     sess = mk.Session(w.shape, w.batch, w.capacity, opts, page_size=page_size, spare_pages=3 if page_size else 0)
     try:
         sess.load(prep.weights)
@@ -237,6 +238,18 @@ def test_dense_parity_persistent(dense):
 def test_dense_parity_launch_per_task(dense):
     w, prep = dense
     reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=2, trace=False)
+    assert_reports(reports)
+
+
+def test_dense_lds_ring_parity(dense):
+    # batch-1 tiles fed through the LDS weight ring (loader wavefronts, LDS-DMA
+    # loads, run-ahead into the next tile): the configured steps with the
+    # ticketed trace, and launch-per-task steps (no run-ahead)
+    w, prep = dense
+    reports, st = run_steps(w, prep, mk.MK_PERSISTENT, steps=w.steps, lds_ring=1)
+    assert st.ring_ops > 0 and st.ring_kb in (2, 4)
+    assert_reports(reports)
+    reports, _ = run_steps(w, prep, mk.MK_LAUNCH_PER_TASK, steps=2, trace=False, lds_ring=1)
     assert_reports(reports)
 
 

@@ -327,3 +327,33 @@ def test_multistep_kv_rows_cross_xcds_only_after_an_ordering_event(wname, steps)
         print(f"{wname}: {reads} in-launch row reads by other chunks, {cross} of them on another XCD")
     finally:
         mk.mk_destroy_graph(g)
+
+
+@pytest.mark.parametrize("wname,batch,kw,ring_kb,ring_ops", [
+    # 8B: rows of 8 KB (K = 4096) and 24 KB (down, K = 12288): 4 KB segments; every GEMV op per layer + lm_head
+    ("qwen3-8b", 1, {"lds_ring": 1}, 4, 36 * 4 + 1),
+    # 0.6B: rows of 2 KB (K = 1024) and 6 KB (down, K = 3072): 2 KB segments
+    ("qwen3-0.6b", 1, {"lds_ring": 1}, 2, 28 * 4 + 1),
+    ("qwen3-1.7b", 1, {"lds_ring": 1}, 4, 28 * 4 + 1),
+    # tiny: 512-byte rows (K = 256) are not whole kilobytes
+    ("tiny", 1, {"lds_ring": 1}, 0, 0),
+    # batch above 1, the MFMA path, and the default (option off): no ring
+    ("qwen3-8b", 2, {"lds_ring": 1}, 0, 0),
+    ("qwen3-8b", 1, {"gemv": mk.MK_GEMV_MFMA, "lds_ring": 1}, 0, 0),
+    ("qwen3-8b", 1, {}, 0, 0),
+])
+def test_lds_ring_assignment(wname, batch, kw, ring_kb, ring_ops):
+    """With lds_ring, batch-1 GEMV tiles with whole-KB rows are fed through
+    the LDS weight ring; one segment size per graph divides every such row."""
+    s = synth.WORKLOADS[wname]
+    g = mk.mk_build_graph(s.shape, batch, s.capacity, mk.make_opts(num_workers=256, **kw))
+    try:
+        st = mk.mk_graph_stats(g)
+        assert (st.ring_kb, st.ring_ops) == (ring_kb, ring_ops)
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+def test_lds_ring_option_is_validated():
+    with pytest.raises(mk.MkError):
+        build(TINY.shape, lds_ring=2)
