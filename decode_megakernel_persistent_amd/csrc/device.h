@@ -712,7 +712,7 @@ DEV void gemv_epilogue(Ctx& c, const OpDesc& op, const float* rsl, int NR, u64 r
 // input words goes out, then the rest of the ring, then the input is staged
 // while the ring streams.  Loads go through a buffer resource so that
 // out-of-range segments return zeros without touching memory.
-constexpr int kEarlySegments = 2;  // segments of wavefront 0 still to consume when an early trigger fires
+constexpr int kEarlySegments = 4;  // segments of wavefront 0 still to consume when an early trigger fires
 template <int NB, int S, int LOADS>
 DEV void gemv_valu(Ctx& c, const OpDesc& op) {
   constexpr int DEPTH = LOADS / S > 1 ? LOADS / S : 2;
