@@ -953,6 +953,62 @@ uint32_t graph_magic(const Graph& g) {
   return h | 1u;
 }
 
+// Odd-numbered XCDs see event counters later and stream weights more slowly
+// than even-numbered ones (measured per XCD from the timing trace: at the 8B
+// batch-1 shape, gate-up tiles on odd XCDs start ~1 us later and run ~9%
+// longer), so the last tile of every operator lands on an odd XCD.  For the
+// O, gate-up, down and lm_head operators of VALU graphs (one dependency event
+// each, so their row split does not change any edge), the rows are re-split
+// after assignment: a tile whose worker w has w mod 8 odd gets
+// opts.xcd_rows_pct percent of the rows of a tile on an even XCD.  Worker w
+// runs on XCD w mod 8 (the device deals workgroups round-robin over the
+// XCDs; the trace records it).  Runs before layout(), which places gate-up
+// weights per tile.  Measured at the 8B batch-1 shape (same box, 64 steps,
+// twice each), equal tiles are fastest: 78% 3.361, 85% 3.341, 92% 3.319,
+// 100% 3.268, 104% 3.273, 108% 3.394, 115% 3.406 ms; the per-XCD lateness
+// follows the contention rather than the work, so equal tiles stay the
+// default and the split is an option.
+constexpr int32_t kDefaultXcdRowsPct = 100;
+static void balance_xcd_rows(Graph& g) {
+  const int32_t pct = g.opts.xcd_rows_pct ? g.opts.xcd_rows_pct : kDefaultXcdRowsPct;
+  if (pct == 100 || g.gemv != MK_GEMV_VALU) return;
+  std::vector<int32_t> worker(g.tasks.size(), -1);
+  for (int32_t w = 0; w < g.W; ++w)
+    for (int32_t k = g.wl_off[w]; k < g.wl_off[w + 1]; ++k) worker[(size_t)g.wl_ids[k]] = w;
+  for (OpInst& op : g.ops) {
+    if (op.kind != OP_OPROJ && op.kind != OP_GATEUP && op.kind != OP_DOWN && op.kind != OP_LMHEAD) continue;
+    const int32_t n = op.ntasks;
+    if (n < 2) continue;
+    int64_t R = 0;
+    std::vector<double> wt((size_t)n);
+    double wsum = 0.0;
+    for (int32_t i = 0; i < n; ++i) {
+      const RawTask& r = g.raw[(size_t)(op.first_raw + i)];
+      R += r.a[2];
+      const int32_t w = worker[(size_t)g.raw_to_id[(size_t)(op.first_raw + i)]];
+      wt[(size_t)i] = (w >= 0 && (w % 8) % 2 == 1) ? pct / 100.0 : 1.0;
+      wsum += wt[(size_t)i];
+    }
+    if (R < n) continue;
+    // contiguous tiles in the original order, sizes proportional to the weights, at least one row each
+    double acc = 0.0;
+    int32_t r0 = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      acc += wt[(size_t)i];
+      int32_t r1 = i + 1 == n ? (int32_t)R : (int32_t)std::llround((double)R * acc / wsum);
+      r1 = std::max(r1, r0 + 1);
+      r1 = std::min<int32_t>(r1, (int32_t)R - (n - 1 - i));
+      RawTask& r = g.raw[(size_t)(op.first_raw + i)];
+      Task& t = g.tasks[(size_t)g.raw_to_id[(size_t)(op.first_raw + i)]];
+      const int32_t a3 = op.kind == OP_GATEUP ? 2 * r0 * op.K : r0 * op.K;
+      r.a[1] = t.a1 = r0;
+      r.a[2] = t.a2 = r1 - r0;
+      r.a[3] = t.a3 = a3;
+      r0 = r1;
+    }
+  }
+}
+
 // With opts.lds_ring, batch-1 VALU GEMV tiles whose rows are whole kilobytes
 // and whose input, segments and rows fit the LDS ring's areas are fed through
 // the LDS weight ring (loader wavefronts stream the weights, see device.h).  The segment
@@ -1011,8 +1067,10 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
   if (batch <= 0 || batch > 16) return bad("batch must be in 1..16");
   if (cap <= 0 || cap > (1 << 20)) return bad("max_ctx out of range");
   if (workers <= 0 || workers > 4096) return bad("worker count out of range");
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 2; ++i)
     if (o.reserved[i]) return bad("reserved options must be zero");
+  if (o.xcd_rows_pct != 0 && (o.xcd_rows_pct < 50 || o.xcd_rows_pct > 150))
+    return bad("xcd_rows_pct must be 0 or in 50..150");
   if (o.lds_ring < 0 || o.lds_ring > 1) return bad("lds_ring must be 0 or 1");
   if (o.prefetch_loads < 0 || o.prefetch_loads > 64) return bad("prefetch_loads must be in 0..64");
   if (o.trace < 0 || o.trace > 2) return bad("trace must be 0, 1 or 2");
@@ -1071,6 +1129,7 @@ Graph* compile_decoder(const mk_model_shape& s, int32_t batch, int32_t cap, cons
     delete g;
     return nullptr;
   }
+  balance_xcd_rows(*g);
   layout(*g);
   Geom& ge = g->geom;
   ge.ring_u = assign_ring(*g);

@@ -107,7 +107,12 @@ typedef struct {
                               ring by four loader wavefronts (LDS-DMA loads) that run ahead into the
                               worker's next tile; 0 = weights stream through registers (default,
                               faster as measured) */
-  int32_t reserved[3];     /* must be zero */
+  int32_t xcd_rows_pct;    /* batch <= 4 VALU GEMV tiles of the O, gate-up, down and lm_head operators:
+                              rows of a tile whose worker runs on an odd-numbered XCD (worker w runs
+                              on XCD w mod 8), in percent of the rows of a tile on an even-numbered
+                              XCD (odd XCDs see events later and stream slower); 0 = default,
+                              100 = equal tiles, else 50..150 */
+  int32_t reserved[2];     /* must be zero */
 } mk_build_opts;
 
 /* One logical tensor handed to mk_load_weights.  Names:

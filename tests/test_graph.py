@@ -357,3 +357,49 @@ def test_lds_ring_assignment(wname, batch, kw, ring_kb, ring_ops):
 def test_lds_ring_option_is_validated():
     with pytest.raises(mk.MkError):
         build(TINY.shape, lds_ring=2)
+
+
+@pytest.mark.parametrize("pct", [100, 85, 120])
+def test_xcd_weighted_row_split(pct):
+    """xcd_rows_pct: the O, gate-up, down and lm_head tiles of a VALU graph
+    still cover their operator's rows exactly once, contiguously in tile
+    order, and a tile whose worker sits on an odd XCD (worker mod 8 odd) gets
+    about pct percent of the rows of an even-XCD tile; weight offsets follow
+    the rows (gate-up tiles hold gate and up rows, two per output row)."""
+    s = synth.WORKLOADS["qwen3-8b"]
+    g = mk.mk_build_graph(s.shape, 1, s.capacity, mk.make_opts(num_workers=256, xcd_rows_pct=pct))
+    try:
+        t = mk.mk_get_tasks(g)
+        off, ids = mk.mk_get_worker_lists(g)
+        worker = np.empty(len(t), np.int64)
+        for w in range(len(off) - 1):
+            worker[ids[off[w]:off[w + 1]]] = w
+        H, I, V = s.shape.hidden, s.shape.intermediate, s.shape.vocab
+        Hq, D = s.shape.n_q_heads, s.shape.head_dim
+        checked = 0
+        for kind, N, K in (("oproj", H, Hq * D), ("gateup", I, H), ("down", H, I), ("lmhead", V, H)):
+            k = mk.OP_KINDS.index(kind)
+            layers = sorted(set(t[t[:, 0] == k][:, 1].tolist()))
+            for layer in layers[:3]:
+                sel = np.nonzero((t[:, 0] == k) & (t[:, 1] == layer))[0]
+                rows = t[sel]
+                order = np.argsort(rows[:, 4])                     # tile order
+                a1, a2, a3 = rows[order, 5], rows[order, 6], rows[order, 7]
+                assert a1[0] == 0 and np.all(a1[1:] == a1[:-1] + a2[:-1]) and a1[-1] + a2[-1] == N
+                assert np.all(a2 >= 1)
+                np.testing.assert_array_equal(a3, a1 * K * (2 if kind == "gateup" else 1))
+                odd = (worker[sel[order]] % 8) % 2 == 1
+                ratio = a2[odd].mean() / a2[~odd].mean()
+                # whole rows: a tile of ~16 rows moves in steps of one row
+                assert abs(ratio - pct / 100.0) < 0.02 + 1.5 / a2.mean(), (kind, layer, ratio)
+                checked += 1
+        assert checked >= 10
+        st = mk.mk_graph_stats(g)
+        assert abs(st.weight_bytes / 1e9 - 15.137) < 0.01
+    finally:
+        mk.mk_destroy_graph(g)
+
+
+def test_xcd_rows_option_is_validated():
+    with pytest.raises(mk.MkError):
+        build(TINY.shape, xcd_rows_pct=20)
