@@ -1271,6 +1271,7 @@ constexpr int kMfmaRS = kMfmaKC + 8;                // staged row stride (bf16 e
 constexpr int kMfmaXBytes = 16 * kMfmaRS * 2;       // one staged part (hi or lo), 16 sequences
 constexpr int kMfmaDepth = 8;     // weight fragments in flight per wavefront
 constexpr int kMfmaMaxItems = 4;  // items per wavefront (row groups per tile <= 32)
+constexpr int kMfmaEarlyTurns = 2;  // ring turns of wavefront 0 left when an early trigger fires
 constexpr int kMfmaVariant = 16;  // kernel template value of the MFMA variant
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 static_assert(NWAVE == 8, "the MFMA stager gives wavefront w sequences w and w + 8");
@@ -1346,6 +1347,7 @@ DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
   const int tid = task_tid(), wave = tid >> 6, lane = tid & 63;
   const int nit = nitems > wave ? (nitems - wave + NWAVE - 1) / NWAVE : 0;
   const int KC = min(kMfmaKC, K), KBc = KC >> 5, nchunks = (K + KC - 1) / KC;
+  const bool early = (op.pad & 2) != 0;  // trigger before the epilogue (tagged outputs)
   constexpr int DEPTH = kMfmaDepth;
   const int NJ = (KBc + kparts - 1) / kparts;
   const int NJp = (NJ + DEPTH - 1) / DEPTH * DEPTH;
@@ -1419,6 +1421,12 @@ DEV void gemv_mfma(Ctx& c, const OpDesc& op) {
             }
             buf[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, fill(), 0, AUX_NT);
           }
+          // early trigger: wavefront 0 in its last item of the last chunk with
+          // kMfmaEarlyTurns ring turns left; consumers that read first find
+          // older tags and re-read (as for the VALU tiles)
+          if (early && wave == 0 && cc == nchunks - 1 && it == nit - 1 && j0 + kMfmaEarlyTurns * DEPTH >= NJp &&
+              lane == 0)
+            trigger_event(c);
         }
       }
     }
